@@ -1,0 +1,107 @@
+"""Scale choice and the fixed-grid quantizer Q_s, written out plainly.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Sources
+  * arXiv 2607.04244, QAD method paragraph: the student keeps the frozen
+    symmetric per-group scales s, its weights W start at s (.) W_q and pass
+    through a fixed-grid fake quantizer Q_s; at packing time the updated
+    bf16 weights are rounded back onto the same grid, giving new INT4 codes
+    under the original scales.
+  * same paper, drafter-PTQ calibration paragraph: group-wise symmetric INT4
+    with group size 128.
+  * Qwen3.5-4B-DFlash-W8A16 model card, "What changed vs upstream" table and
+    the recipe paragraph below it: int8 weight-only, RTN, symmetric,
+    group = 128, bf16 scales, no calibration data.
+
+Readings taken where the pages are silent (each is listed in the design
+notes of the repository):
+  * groups run along K (the input-feature axis), one scale per (group, output
+    column); scales are stored [K/128, N];
+  * INT4 codes lie in [-8, 7], INT8 codes in [-127, 127];
+  * RTN picks s = max|w| / 7 (INT4) or max|w| / 127 (INT8), divided in fp32
+    and stored as fp16 (INT4) or bf16 (INT8) with RNE; a NaN weight counts as
+    0 for the maximum;
+  * Q_s divides in fp32 with IEEE (correctly rounded) division -- never a
+    multiply by a reciprocal -- rounds the quotient to nearest with ties to
+    even, then clamps; a zero scale or a NaN quotient gives code 0 and an
+    infinite quotient saturates to the end of the range.
+"""
+
+import numpy as np
+
+from . import numerics
+
+GROUP = 128
+
+RANGE = {4: (-8, 7), 8: (-127, 127)}
+RTN_DIVISOR = {4: 7.0, 8: 127.0}
+SCALE_DTYPE = {4: "f16", 8: "bf16"}
+
+
+def group_count(K):
+    if K % GROUP:
+        raise ValueError("K must be a multiple of 128")
+    return K // GROUP
+
+
+def expand_groups(s, K):
+    """Repeat a [K/128, N] per-group array along K to [K, N]."""
+    return np.repeat(np.asarray(s), GROUP, axis=0)[:K]
+
+
+def rtn_scales(W, bits):
+    """Round-to-nearest scale choice; returns stored scale bit patterns.
+
+    W: float32 [K, N]. For each group g and column n the scale is the largest
+    magnitude in W[128g : 128g+128, n] divided (fp32) by 7 or 127, rounded to
+    fp16 (bits=4) or bf16 (bits=8). Returns uint16 [K/128, N].
+    """
+    W = np.asarray(W, dtype=np.float32)
+    K, N = W.shape
+    G = group_count(K)
+    mag = np.abs(W)
+    mag = np.where(np.isnan(mag), np.float32(0.0), mag)
+    amax = mag.reshape(G, GROUP, N).max(axis=1).astype(np.float32)
+    with np.errstate(over="ignore", invalid="ignore"):
+        s32 = amax / np.float32(RTN_DIVISOR[bits])
+    if bits == 4:
+        return numerics.f32_to_f16(s32)
+    return numerics.f32_to_bf16(s32)
+
+
+def q_s(W, scale_values, bits):
+    """Fixed-grid quantizer: codes = clamp(rne(W / s), lo, hi).
+
+    W: float32 [K, N] (bf16 weights are passed as their exact fp32 values).
+    scale_values: the stored scales decoded to real numbers, [K/128, N].
+    Returns int8 codes [K, N].
+    """
+    W = np.asarray(W, dtype=np.float32)
+    K, _ = W.shape
+    s = expand_groups(np.asarray(scale_values, dtype=np.float64), K).astype(np.float32)
+    lo, hi = RANGE[bits]
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        t = W / s                         # IEEE fp32 division, elementwise
+    q = np.rint(t)                        # ties to even
+    q = np.clip(q, lo, hi)
+    q = np.where((s == 0) | np.isnan(t), 0.0, q)
+    return q.astype(np.int8)
+
+
+def rtn_quantize(W, bits):
+    """RTN from scratch: scales from the weights, then Q_s under them.
+
+    Returns (codes int8 [K,N], scale bit patterns uint16 [K/128,N]).
+    """
+    sb = rtn_scales(W, bits)
+    sv = numerics.scale_bits_to_f64(sb, SCALE_DTYPE[bits])
+    return q_s(W, sv, bits), sb
+
+
+def dequant(codes, scale_values):
+    """s (.) W_q as float64: every element is exact (at most 15 significant
+    bits: an 11-bit fp16 or 8-bit bf16 scale times a code of magnitude <= 127).
+    """
+    c = np.asarray(codes).astype(np.float64)
+    return c * expand_groups(np.asarray(scale_values, dtype=np.float64), c.shape[0])
