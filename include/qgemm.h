@@ -1,0 +1,173 @@
+/*
+ * qgemm.h -- weight-only group-quantized matrix multiply for AMD Instinct
+ * MI355X (gfx950), C ABI.
+ *
+ * What is computed
+ *   A quantized Linear y = x . W with W stored as integer codes W_q and one
+ *   scale per group of 128 consecutive input features per output column; the
+ *   effective weight is the dequantized s (.) W_q ("Quantize the Target,
+ *   Quantize the Drafter", arXiv 2607.04244, QAD method paragraph; group-wise
+ *   symmetric INT4 with group size 128, drafter-PTQ calibration paragraph).
+ *   INT4 codes with fp16 scales serve the W4A16 target and drafter (same
+ *   paper; the quickstart of the Qwen3.5-4B-DFlash-GPTQ-W4A16 model card);
+ *   INT8 codes with bf16 scales are the W8A16 variant (Qwen3.5-4B-DFlash-W8A16
+ *   model card, "What changed vs upstream" table). The fixed-grid quantizer
+ *   Q_s puts updated weights back on the frozen grid (QAD method paragraph:
+ *   at packing time the updated bf16 weights are rounded onto the same grid,
+ *   giving new codes under the original scales).
+ *
+ * Conventions shared by every entry point
+ *   - Logical layouts are row-major and contiguous:
+ *       x[M,K] bf16, out[M,N] bf16, W[K,N], codes[K,N] int8,
+ *       scales[K/128, N] (fp16 or bf16).
+ *     A PyTorch Linear weight is [N,K]; transpose it before packing.
+ *   - K must be a positive multiple of 128 and N a positive multiple of 16,
+ *     else QG_ERR_SHAPE. M may be 0 (nothing is launched). Limits:
+ *     K, N <= 2^20, M <= 2^24, and M*K, M*N, K*N each < 2^31.
+ *   - Every pointer is a DEVICE pointer owned by the caller, 16-byte aligned
+ *     (else QG_ERR_ALIGN), non-NULL when its size is non-zero (else
+ *     QG_ERR_NULL). Outputs must not alias inputs. The library allocates no
+ *     device memory and frees nothing.
+ *   - stream is a hipStream_t (NULL = the default stream). Calls enqueue work
+ *     on it and return without waiting. Argument checks run on the host
+ *     before any HIP call; on any error nothing is enqueued and no output is
+ *     touched. A failed launch returns QG_ERR_HIP. No C++ exception crosses
+ *     this interface.
+ *   - Identical inputs give bit-identical outputs: no reduction depends on
+ *     the order in which workgroups finish.
+ *
+ * Packed-weight layout (the pages name only the container, "compressed-
+ * tensors pack-quantized", with no bit layout, so this one is the library's
+ * own). Codes are cut into tiles of 16 output columns x 128 K (one group).
+ * Tile t = (n/16) * (K/128) + k/128. Inside a tile, lane l in [0,64) owns
+ * column 16*(n/16) + l%16 and, for K step j in [0,4) and element i in [0,8),
+ * k = 128*(k/128) + 32*j + 8*(l/16) + i -- the B-operand order of the
+ * 16x16x32 bf16 matrix-core instruction.
+ *   INT4: tile = 1024 bytes; lane l's K step j is the little-endian 32-bit
+ *         word at byte 1024*t + 16*l + 4*j; element i is the nibble at bits
+ *         4*p..4*p+3 with p = i/2 + 4*(i%2); the nibble holds q + 8.
+ *   INT8: tile = 2048 bytes; element i of K step j of lane l is the byte at
+ *         2048*t + 32*l + 8*j + i, holding q in two's complement.
+ */
+#ifndef QGEMM_H
+#define QGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QG_OK = 0,
+  QG_ERR_NULL = 1,      /* a required pointer is NULL                      */
+  QG_ERR_SHAPE = 2,     /* K, N or M outside the rules above               */
+  QG_ERR_ALIGN = 3,     /* a pointer is not 16-byte aligned                */
+  QG_ERR_DTYPE = 4,     /* unsupported dtype enum for that argument        */
+  QG_ERR_WORKSPACE = 5, /* workspace missing or smaller than required      */
+  QG_ERR_HIP = 6,       /* the HIP runtime reported an error at launch     */
+  QG_ERR_PLAN = 7       /* an explicit tiling plan is not supported        */
+} qg_status;
+
+typedef enum { QG_BF16 = 0, QG_F16 = 1, QG_F32 = 2 } qg_dtype;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* qg_status_str(qg_status s);
+
+/* Bytes of packed codes for a [K,N] weight: K*N/2 (bits=4) or K*N (bits=8);
+ * 0 for an invalid shape or bit width. */
+size_t qg_packed_bytes(int bits, int64_t K, int64_t N);
+
+/* Bytes of the [K/128, N] scale array (2 bytes per scale). */
+size_t qg_scale_bytes(int64_t K, int64_t N);
+
+/* Workspace the GEMM needs for this shape (split-K partial sums and arrival
+ * counters); 0 when the chosen plan needs none. The first 65536 bytes of a
+ * workspace hold arrival counters: they must be zero before the first call
+ * that uses the workspace, and every completed call leaves them zero again
+ * (the rest holds fp32 partial sums and needs no initial value). Calls that
+ * share one workspace must not overlap in time (use one stream or distinct
+ * workspaces). */
+size_t qg_workspace_bytes(int bits, int64_t M, int64_t K, int64_t N);
+
+/* RTN scale choice from the weights, no calibration data (W8A16 model card:
+ * RTN, symmetric, group = 128, "pure RTN on the weights").
+ *   W        [K,N], w_dt = QG_F32 or QG_BF16
+ *   scales   [K/128,N] out: fp16 max|w|/7 (w4) or bf16 max|w|/127 (w8),
+ *            fp32 division rounded to nearest even; NaN weights count as 0. */
+qg_status qg_rtn_scales_w4(const void* W, qg_dtype w_dt, int64_t K, int64_t N,
+                           void* scales, void* stream);
+qg_status qg_rtn_scales_w8(const void* W, qg_dtype w_dt, int64_t K, int64_t N,
+                           void* scales, void* stream);
+
+/* Fixed-grid quantizer Q_s plus packing (QAD method paragraph of arXiv
+ * 2607.04244: updated bf16 weights rounded back onto the frozen grid).
+ *   W        [K,N], w_dt = QG_F32 or QG_BF16
+ *   scales   [K/128,N], s_dt = QG_F16 or QG_BF16 -- inputs, never recomputed
+ *   packed_w out, qg_packed_bytes(bits,K,N) bytes in the layout above
+ * code = clamp(rne(W / s), lo, hi) with IEEE fp32 division; (lo,hi) = (-8,7)
+ * for w4 and (-127,127) for w8; s == 0 or a NaN quotient gives 0; an
+ * infinite quotient saturates. */
+qg_status qg_pack_to_grid_w4(const void* W, qg_dtype w_dt, const void* scales,
+                             qg_dtype s_dt, int64_t K, int64_t N,
+                             void* packed_w, void* stream);
+qg_status qg_pack_to_grid_w8(const void* W, qg_dtype w_dt, const void* scales,
+                             qg_dtype s_dt, int64_t K, int64_t N,
+                             void* packed_w, void* stream);
+
+/* Reorder logical int8 codes [K,N] into the packed layout, and back.
+ * prepack_w4 stores the low 4 bits of q + 8, so codes outside [-8,7] do not
+ * survive the round trip; prepack_w8 stores q unchanged. unpack is the exact
+ * inverse of prepack on in-range codes. */
+qg_status qg_prepack_w4(const int8_t* codes, int64_t K, int64_t N,
+                        void* packed_w, void* stream);
+qg_status qg_unpack_w4(const void* packed_w, int64_t K, int64_t N,
+                       int8_t* codes, void* stream);
+qg_status qg_prepack_w8(const int8_t* codes, int64_t K, int64_t N,
+                        void* packed_w, void* stream);
+qg_status qg_unpack_w8(const void* packed_w, int64_t K, int64_t N,
+                       int8_t* codes, void* stream);
+
+/* out[M,N] = bf16_rne( x[M,K] . (s (.) W_q) ), fp32 accumulation.
+ *   x         bf16 [M,K]
+ *   packed_w  qg_packed_bytes(bits,K,N) bytes (from pack_to_grid or prepack)
+ *   scales    [K/128,N]; s_dt = QG_F16 or QG_BF16
+ *   out       bf16 [M,N]
+ *   workspace qg_workspace_bytes(bits,M,K,N) bytes (may be NULL when 0);
+ *             see qg_workspace_bytes for the zero-counter rule.
+ * Products of activations and codes are exact; each group of 128 is summed
+ * in fp32, multiplied by its fp32 scale and added to an fp32 accumulator.
+ * Supported domain: |x| < 1e30 (the int4 path carries a bias of 136 per
+ * code through fp32 sums). */
+qg_status qgemm_w4a16(const void* x, const void* packed_w, const void* scales,
+                      qg_dtype s_dt, void* out, int64_t M, int64_t K, int64_t N,
+                      void* workspace, size_t workspace_bytes, void* stream);
+qg_status qgemm_w8a16(const void* x, const void* packed_w, const void* scales,
+                      qg_dtype s_dt, void* out, int64_t M, int64_t K, int64_t N,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* The same GEMMs with an explicit small-M tiling plan, for tests and tuning.
+ *   cols_per_wave  16-column blocks per wavefront: 1, 2 or 4
+ *   k_waves        wavefronts of a workgroup that split K: 1, 2 or 4
+ *   splits         workgroups that split K (>= 1, at most K/128)
+ * Any argument 0 takes the library's choice. Unsupported values give
+ * QG_ERR_PLAN. workspace must cover qg_workspace_bytes_plan(). */
+qg_status qgemm_w4a16_plan(const void* x, const void* packed_w,
+                           const void* scales, qg_dtype s_dt, void* out,
+                           int64_t M, int64_t K, int64_t N, void* workspace,
+                           size_t workspace_bytes, int cols_per_wave,
+                           int k_waves, int splits, void* stream);
+qg_status qgemm_w8a16_plan(const void* x, const void* packed_w,
+                           const void* scales, qg_dtype s_dt, void* out,
+                           int64_t M, int64_t K, int64_t N, void* workspace,
+                           size_t workspace_bytes, int cols_per_wave,
+                           int k_waves, int splits, void* stream);
+size_t qg_workspace_bytes_plan(int bits, int64_t M, int64_t K, int64_t N,
+                               int cols_per_wave, int k_waves, int splits);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGEMM_H */

@@ -1,0 +1,217 @@
+"""Thin Python binding over libqgemm.so (the C ABI in include/qgemm.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of the library. Tensors are PyTorch CUDA (HIP) tensors; work is
+enqueued on the current PyTorch stream of the tensor's device. If the
+library has not been built this module raises at first use -- there is no
+fallback path.
+"""
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqgemm.so")
+_lib = None
+_lock = threading.Lock()
+
+QG_BF16, QG_F16, QG_F32 = 0, 1, 2
+STATUS = {0: "QG_OK", 1: "QG_ERR_NULL", 2: "QG_ERR_SHAPE", 3: "QG_ERR_ALIGN",
+          4: "QG_ERR_DTYPE", 5: "QG_ERR_WORKSPACE", 6: "QG_ERR_HIP", 7: "QG_ERR_PLAN"}
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_INT = ctypes.c_int
+_SZ = ctypes.c_size_t
+
+_SIGNATURES = {
+    "qg_status_str": ([_INT], ctypes.c_char_p),
+    "qg_packed_bytes": ([_INT, _I64, _I64], _SZ),
+    "qg_scale_bytes": ([_I64, _I64], _SZ),
+    "qg_workspace_bytes": ([_INT, _I64, _I64, _I64], _SZ),
+    "qg_workspace_bytes_plan": ([_INT, _I64, _I64, _I64, _INT, _INT, _INT], _SZ),
+    "qg_rtn_scales_w4": ([_P, _INT, _I64, _I64, _P, _P], _INT),
+    "qg_rtn_scales_w8": ([_P, _INT, _I64, _I64, _P, _P], _INT),
+    "qg_pack_to_grid_w4": ([_P, _INT, _P, _INT, _I64, _I64, _P, _P], _INT),
+    "qg_pack_to_grid_w8": ([_P, _INT, _P, _INT, _I64, _I64, _P, _P], _INT),
+    "qg_prepack_w4": ([_P, _I64, _I64, _P, _P], _INT),
+    "qg_unpack_w4": ([_P, _I64, _I64, _P, _P], _INT),
+    "qg_prepack_w8": ([_P, _I64, _I64, _P, _P], _INT),
+    "qg_unpack_w8": ([_P, _I64, _I64, _P, _P], _INT),
+    "qgemm_w4a16": ([_P, _P, _P, _INT, _P, _I64, _I64, _I64, _P, _SZ, _P], _INT),
+    "qgemm_w8a16": ([_P, _P, _P, _INT, _P, _I64, _I64, _I64, _P, _SZ, _P], _INT),
+    "qgemm_w4a16_plan": ([_P, _P, _P, _INT, _P, _I64, _I64, _I64, _P, _SZ, _INT, _INT, _INT, _P],
+                         _INT),
+    "qgemm_w8a16_plan": ([_P, _P, _P, _INT, _P, _I64, _I64, _I64, _P, _SZ, _INT, _INT, _INT, _P],
+                         _INT),
+}
+
+
+class QGError(RuntimeError):
+    def __init__(self, fn, code):
+        super().__init__("%s failed: %s" % (fn, STATUS.get(code, code)))
+        self.code = code
+
+
+def lib():
+    """Load libqgemm.so (once). Raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB_PATH):
+                raise RuntimeError(
+                    "libqgemm.so is not built; run `python -m int8_group_quantized_amd.build`")
+            L = ctypes.CDLL(_LIB_PATH)
+            for name, (args, res) in _SIGNATURES.items():
+                f = getattr(L, name)
+                f.argtypes = args
+                f.restype = res
+            _lib = L
+    return _lib
+
+
+def library_path():
+    return _LIB_PATH
+
+
+def _check(fn, code):
+    if code != 0:
+        raise QGError(fn, code)
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _dt(t):
+    if t.dtype == torch.bfloat16:
+        return QG_BF16
+    if t.dtype == torch.float16:
+        return QG_F16
+    if t.dtype == torch.float32:
+        return QG_F32
+    raise TypeError("unsupported dtype %s" % t.dtype)
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("tensors must be contiguous GPU tensors")
+
+
+def packed_bytes(bits, K, N):
+    return int(lib().qg_packed_bytes(bits, K, N))
+
+
+def workspace_bytes(bits, M, K, N, plan=None):
+    if plan is None:
+        return int(lib().qg_workspace_bytes(bits, M, K, N))
+    return int(lib().qg_workspace_bytes_plan(bits, M, K, N, *plan))
+
+
+# Zero-initialised workspace per device, grown on demand. The library leaves
+# its arrival counters at zero after every call, so the buffer is reusable on
+# one stream.
+_workspaces = {}
+
+
+def workspace(device, nbytes):
+    device = torch.device(device)
+    key = device.index if device.index is not None else torch.cuda.current_device()
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def rtn_scales(W, bits):
+    """RTN scales [K/128, N]: fp16 (bits=4) or bf16 (bits=8)."""
+    _need_cuda(W)
+    K, N = W.shape
+    s = torch.empty((K // 128, N), dtype=torch.float16 if bits == 4 else torch.bfloat16,
+                    device=W.device)
+    fn = "qg_rtn_scales_w%d" % bits
+    _check(fn, getattr(lib(), fn)(_ptr(W), _dt(W), K, N, _ptr(s), _stream(W)))
+    return s
+
+
+def pack_to_grid(W, scales, bits):
+    """Q_s(W) under the given scales, packed; returns a uint8 tensor."""
+    _need_cuda(W, scales)
+    K, N = W.shape
+    out = torch.empty(packed_bytes(bits, K, N), dtype=torch.uint8, device=W.device)
+    fn = "qg_pack_to_grid_w%d" % bits
+    _check(fn, getattr(lib(), fn)(_ptr(W), _dt(W), _ptr(scales), _dt(scales), K, N, _ptr(out),
+                                  _stream(W)))
+    return out
+
+
+def pack_to_grid_w4(W, scales):
+    return pack_to_grid(W, scales, 4)
+
+
+def pack_to_grid_w8(W, scales):
+    return pack_to_grid(W, scales, 8)
+
+
+def prepack(codes, bits):
+    _need_cuda(codes)
+    if codes.dtype != torch.int8:
+        raise TypeError("codes must be int8")
+    K, N = codes.shape
+    out = torch.empty(packed_bytes(bits, K, N), dtype=torch.uint8, device=codes.device)
+    fn = "qg_prepack_w%d" % bits
+    _check(fn, getattr(lib(), fn)(_ptr(codes), K, N, _ptr(out), _stream(codes)))
+    return out
+
+
+def unpack(packed, K, N, bits):
+    _need_cuda(packed)
+    codes = torch.empty((K, N), dtype=torch.int8, device=packed.device)
+    fn = "qg_unpack_w%d" % bits
+    _check(fn, getattr(lib(), fn)(_ptr(packed), K, N, _ptr(codes), _stream(packed)))
+    return codes
+
+
+def qgemm(x, packed_w, scales, bits, N, out=None, plan=None, ws=None):
+    """out[M,N] = x[M,K] . (s (.) W_q) in bf16 with fp32 accumulation.
+
+    plan: optional (cols_per_wave, k_waves, splits) for the small-M kernel.
+    ws: optional workspace tensor (zeroed before first use).
+    """
+    _need_cuda(x, packed_w, scales, out)
+    if x.dtype != torch.bfloat16:
+        raise TypeError("x must be bf16")
+    M, K = x.shape
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    need = workspace_bytes(bits, M, K, N, plan)
+    if ws is None and need > 0:
+        ws = workspace(x.device, need)
+    ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
+    if plan is None:
+        fn = "qgemm_w%da16" % bits
+        code = getattr(lib(), fn)(_ptr(x), _ptr(packed_w), _ptr(scales), _dt(scales), _ptr(out),
+                                  M, K, N, _ptr(ws), ws_bytes, _stream(x))
+    else:
+        fn = "qgemm_w%da16_plan" % bits
+        code = getattr(lib(), fn)(_ptr(x), _ptr(packed_w), _ptr(scales), _dt(scales), _ptr(out),
+                                  M, K, N, _ptr(ws), ws_bytes, plan[0], plan[1], plan[2],
+                                  _stream(x))
+    _check(fn, code)
+    return out
+
+
+def qgemm_w4a16(x, packed_w, scales, N, out=None, plan=None, ws=None):
+    return qgemm(x, packed_w, scales, 4, N, out=out, plan=plan, ws=ws)
+
+
+def qgemm_w8a16(x, packed_w, scales, N, out=None, plan=None, ws=None):
+    return qgemm(x, packed_w, scales, 8, N, out=out, plan=plan, ws=ws)

@@ -1,0 +1,211 @@
+// C ABI of the library (declared in include/qgemm.h). Every entry point
+// checks its arguments on the host, before any HIP call, and only then
+// enqueues work on the caller's stream. Nothing here allocates device memory.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "qg_internal.h"
+#include "qgemm.h"
+
+namespace {
+
+constexpr int64_t kMaxKN = int64_t(1) << 20;
+constexpr int64_t kMaxM = int64_t(1) << 24;
+constexpr int64_t kMaxElems = int64_t(1) << 31;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+qg_status check_kn(int64_t K, int64_t N) {
+  if (K <= 0 || N <= 0 || K % 128 != 0 || N % 16 != 0) return QG_ERR_SHAPE;
+  if (K > kMaxKN || N > kMaxKN || K * N >= kMaxElems) return QG_ERR_SHAPE;
+  return QG_OK;
+}
+
+qg_status check_mkn(int64_t M, int64_t K, int64_t N) {
+  const qg_status s = check_kn(K, N);
+  if (s != QG_OK) return s;
+  if (M < 0 || M > kMaxM || M * K >= kMaxElems || M * N >= kMaxElems) return QG_ERR_SHAPE;
+  return QG_OK;
+}
+
+// NULL first, then alignment, over a list of pointers.
+qg_status check_ptrs(std::initializer_list<const void*> ptrs) {
+  for (const void* p : ptrs)
+    if (p == nullptr) return QG_ERR_NULL;
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return QG_ERR_ALIGN;
+  return QG_OK;
+}
+
+qg_status from_hip(hipError_t e) { return e == hipSuccess ? QG_OK : QG_ERR_HIP; }
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+qg_status rtn_scales(int bits, const void* W, qg_dtype w_dt, int64_t K, int64_t N, void* scales,
+                     void* stream) {
+  qg_status s = check_kn(K, N);
+  if (s != QG_OK) return s;
+  if (w_dt != QG_F32 && w_dt != QG_BF16) return QG_ERR_DTYPE;
+  if ((s = check_ptrs({W, scales})) != QG_OK) return s;
+  return from_hip(qg::launch_rtn_scales(bits, W, w_dt == QG_BF16, K, N, scales, as_stream(stream)));
+}
+
+qg_status pack_to_grid(int bits, const void* W, qg_dtype w_dt, const void* scales, qg_dtype s_dt,
+                       int64_t K, int64_t N, void* packed, void* stream) {
+  qg_status s = check_kn(K, N);
+  if (s != QG_OK) return s;
+  if (w_dt != QG_F32 && w_dt != QG_BF16) return QG_ERR_DTYPE;
+  if (s_dt != QG_F16 && s_dt != QG_BF16) return QG_ERR_DTYPE;
+  if ((s = check_ptrs({W, scales, packed})) != QG_OK) return s;
+  return from_hip(qg::launch_pack_to_grid(bits, W, w_dt == QG_BF16, scales, s_dt == QG_BF16, K, N,
+                                          packed, as_stream(stream)));
+}
+
+qg_status prepack(int bits, const int8_t* codes, int64_t K, int64_t N, void* packed, void* stream) {
+  qg_status s = check_kn(K, N);
+  if (s != QG_OK) return s;
+  if ((s = check_ptrs({codes, packed})) != QG_OK) return s;
+  return from_hip(qg::launch_prepack(bits, codes, K, N, packed, as_stream(stream)));
+}
+
+qg_status unpack(int bits, const void* packed, int64_t K, int64_t N, int8_t* codes, void* stream) {
+  qg_status s = check_kn(K, N);
+  if (s != QG_OK) return s;
+  if ((s = check_ptrs({packed, codes})) != QG_OK) return s;
+  return from_hip(qg::launch_unpack(bits, packed, K, N, codes, as_stream(stream)));
+}
+
+qg_status gemm(int bits, const void* x, const void* packed, const void* scales, qg_dtype s_dt,
+               void* out, int64_t M, int64_t K, int64_t N, void* ws, size_t ws_bytes, int nbw,
+               int wk, int splits, void* stream) {
+  qg_status s = check_mkn(M, K, N);
+  if (s != QG_OK) return s;
+  if (s_dt != QG_F16 && s_dt != QG_BF16) return QG_ERR_DTYPE;
+  if ((s = check_ptrs({packed, scales})) != QG_OK) return s;
+  if (M == 0) return QG_OK;
+  if ((s = check_ptrs({x, out})) != QG_OK) return s;
+  qg::SmallPlan plan;
+  if (!qg::make_small_plan(bits, M, K, N, nbw, wk, splits, &plan)) return QG_ERR_PLAN;
+  const size_t need = qg::small_plan_workspace(plan, M, N);
+  if (need > 0) {
+    if (ws == nullptr || ws_bytes < need) return QG_ERR_WORKSPACE;
+    if (!aligned16(ws)) return QG_ERR_ALIGN;
+  }
+  return from_hip(qg::launch_gemm_small(bits, plan, x, packed, scales, s_dt == QG_BF16, out, M, K,
+                                        N, ws, as_stream(stream)));
+}
+
+size_t workspace_bytes(int bits, int64_t M, int64_t K, int64_t N, int nbw, int wk, int splits) {
+  if ((bits != 4 && bits != 8) || check_mkn(M, K, N) != QG_OK || M == 0) return 0;
+  qg::SmallPlan plan;
+  if (!qg::make_small_plan(bits, M, K, N, nbw, wk, splits, &plan)) return 0;
+  return qg::small_plan_workspace(plan, M, N);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qg_status_str(qg_status s) {
+  switch (s) {
+    case QG_OK: return "QG_OK";
+    case QG_ERR_NULL: return "QG_ERR_NULL: a required pointer is NULL";
+    case QG_ERR_SHAPE: return "QG_ERR_SHAPE: K must be a positive multiple of 128, N of 16, within limits";
+    case QG_ERR_ALIGN: return "QG_ERR_ALIGN: pointers must be 16-byte aligned";
+    case QG_ERR_DTYPE: return "QG_ERR_DTYPE: unsupported dtype for this argument";
+    case QG_ERR_WORKSPACE: return "QG_ERR_WORKSPACE: workspace missing or too small";
+    case QG_ERR_HIP: return "QG_ERR_HIP: the HIP runtime reported an error";
+    case QG_ERR_PLAN: return "QG_ERR_PLAN: unsupported tiling plan";
+  }
+  return "unknown qg_status";
+}
+
+size_t qg_packed_bytes(int bits, int64_t K, int64_t N) {
+  if (check_kn(K, N) != QG_OK) return 0;
+  if (bits == 4) return (size_t)(K * N / 2);
+  if (bits == 8) return (size_t)(K * N);
+  return 0;
+}
+
+size_t qg_scale_bytes(int64_t K, int64_t N) {
+  if (check_kn(K, N) != QG_OK) return 0;
+  return (size_t)(K / 128 * N * 2);
+}
+
+size_t qg_workspace_bytes(int bits, int64_t M, int64_t K, int64_t N) {
+  return workspace_bytes(bits, M, K, N, 0, 0, 0);
+}
+
+size_t qg_workspace_bytes_plan(int bits, int64_t M, int64_t K, int64_t N, int cols_per_wave,
+                               int k_waves, int splits) {
+  return workspace_bytes(bits, M, K, N, cols_per_wave, k_waves, splits);
+}
+
+qg_status qg_rtn_scales_w4(const void* W, qg_dtype w_dt, int64_t K, int64_t N, void* scales,
+                           void* stream) {
+  return rtn_scales(4, W, w_dt, K, N, scales, stream);
+}
+
+qg_status qg_rtn_scales_w8(const void* W, qg_dtype w_dt, int64_t K, int64_t N, void* scales,
+                           void* stream) {
+  return rtn_scales(8, W, w_dt, K, N, scales, stream);
+}
+
+qg_status qg_pack_to_grid_w4(const void* W, qg_dtype w_dt, const void* scales, qg_dtype s_dt,
+                             int64_t K, int64_t N, void* packed_w, void* stream) {
+  return pack_to_grid(4, W, w_dt, scales, s_dt, K, N, packed_w, stream);
+}
+
+qg_status qg_pack_to_grid_w8(const void* W, qg_dtype w_dt, const void* scales, qg_dtype s_dt,
+                             int64_t K, int64_t N, void* packed_w, void* stream) {
+  return pack_to_grid(8, W, w_dt, scales, s_dt, K, N, packed_w, stream);
+}
+
+qg_status qg_prepack_w4(const int8_t* codes, int64_t K, int64_t N, void* packed_w, void* stream) {
+  return prepack(4, codes, K, N, packed_w, stream);
+}
+
+qg_status qg_unpack_w4(const void* packed_w, int64_t K, int64_t N, int8_t* codes, void* stream) {
+  return unpack(4, packed_w, K, N, codes, stream);
+}
+
+qg_status qg_prepack_w8(const int8_t* codes, int64_t K, int64_t N, void* packed_w, void* stream) {
+  return prepack(8, codes, K, N, packed_w, stream);
+}
+
+qg_status qg_unpack_w8(const void* packed_w, int64_t K, int64_t N, int8_t* codes, void* stream) {
+  return unpack(8, packed_w, K, N, codes, stream);
+}
+
+qg_status qgemm_w4a16(const void* x, const void* packed_w, const void* scales, qg_dtype s_dt,
+                      void* out, int64_t M, int64_t K, int64_t N, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  return gemm(4, x, packed_w, scales, s_dt, out, M, K, N, workspace, workspace_bytes, 0, 0, 0,
+              stream);
+}
+
+qg_status qgemm_w8a16(const void* x, const void* packed_w, const void* scales, qg_dtype s_dt,
+                      void* out, int64_t M, int64_t K, int64_t N, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  return gemm(8, x, packed_w, scales, s_dt, out, M, K, N, workspace, workspace_bytes, 0, 0, 0,
+              stream);
+}
+
+qg_status qgemm_w4a16_plan(const void* x, const void* packed_w, const void* scales, qg_dtype s_dt,
+                           void* out, int64_t M, int64_t K, int64_t N, void* workspace,
+                           size_t workspace_bytes, int cols_per_wave, int k_waves, int splits,
+                           void* stream) {
+  return gemm(4, x, packed_w, scales, s_dt, out, M, K, N, workspace, workspace_bytes,
+              cols_per_wave, k_waves, splits, stream);
+}
+
+qg_status qgemm_w8a16_plan(const void* x, const void* packed_w, const void* scales, qg_dtype s_dt,
+                           void* out, int64_t M, int64_t K, int64_t N, void* workspace,
+                           size_t workspace_bytes, int cols_per_wave, int k_waves, int splits,
+                           void* stream) {
+  return gemm(8, x, packed_w, scales, s_dt, out, M, K, N, workspace, workspace_bytes,
+              cols_per_wave, k_waves, splits, stream);
+}
+
+}  // extern "C"

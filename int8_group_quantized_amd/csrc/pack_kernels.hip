@@ -1,0 +1,226 @@
+// Elementwise, HBM-bound kernels around the packed layout:
+//   rtn_scales     per-group RTN scale from the weights
+//                  (W8A16 model card: RTN, symmetric, group = 128)
+//   pack_to_grid   the fixed-grid quantizer Q_s + packing
+//                  (arXiv 2607.04244, QAD paragraph: updated bf16 weights
+//                  rounded back onto the frozen grid)
+//   prepack/unpack reorder logical codes into / out of the packed tiles
+//
+// Thread mapping for the tile kernels: one thread per (tile, lane), i.e. per
+// 16 packed bytes (INT4) or 32 (INT8). A thread's 32 codes share one column
+// and one group, hence one scale. Packed stores are 16-byte vector stores,
+// contiguous across the wavefront (one 1 KiB or 2 KiB tile per wave).
+#include "qg_device.h"
+#include "qg_internal.h"
+
+namespace qg {
+namespace {
+
+template <bool W_BF16>
+__device__ __forceinline__ float load_weight(const void* W, int64_t idx) {
+  if constexpr (W_BF16) {
+    return bf16_bits_to_f32(static_cast<const uint16_t*>(W)[idx]);
+  } else {
+    return static_cast<const float*>(W)[idx];
+  }
+}
+
+// Nibble position (within a 32-bit word) of element i of an 8-deep slice.
+__device__ __forceinline__ constexpr int nibble_of(int i) { return (i >> 1) + 4 * (i & 1); }
+
+// scales[g, n] for every (g, n): max |W[128g .. 128g+127, n]| / divisor.
+template <int BITS, bool W_BF16>
+__global__ __launch_bounds__(256) void rtn_scales_kernel(const void* __restrict__ W,
+                                                         uint16_t* __restrict__ scales,
+                                                         int K, int N) {
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  const int g = blockIdx.y;
+  if (n >= N) return;
+  float amax = 0.0f;
+  const int64_t base = (int64_t)g * kGroup * N + n;
+#pragma unroll 8
+  for (int r = 0; r < kGroup; ++r) {
+    float a = fabsf(load_weight<W_BF16>(W, base + (int64_t)r * N));
+    a = (a != a) ? 0.0f : a;          // NaN weights count as 0
+    amax = fmaxf(amax, a);
+  }
+  const float s = amax / (BITS == 4 ? 7.0f : 127.0f);   // IEEE division
+  scales[(int64_t)g * N + n] = (BITS == 4) ? f32_to_f16_bits(s) : f32_to_bf16_bits(s);
+}
+
+// Gather the 32 logical values of one (tile, lane) in element order:
+// v[j*8 + i] is k = 128g + 32j + 8*(lane/16) + i, column 16*nb + lane%16.
+struct LaneCoords {
+  int64_t col;      // n
+  int64_t row0;     // k of element (j=0, i=0)
+  int64_t out_u4;   // index of the lane's first 16-byte word in the packed array
+  int g;
+};
+
+template <int BITS>
+__device__ __forceinline__ bool lane_coords(int K, int N, LaneCoords* c) {
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int G = K / kGroup;
+  const int64_t tiles = (int64_t)(N / kTileCols) * G;
+  const int64_t tile = gid >> 6;
+  if (tile >= tiles) return false;
+  const int lane = (int)(gid & 63);
+  const int64_t nb = tile / G;
+  c->g = (int)(tile - nb * G);
+  c->col = nb * kTileCols + (lane & 15);
+  c->row0 = (int64_t)c->g * kGroup + 8 * (lane >> 4);
+  c->out_u4 = (BITS == 4) ? gid : 2 * gid;
+  return true;
+}
+
+template <int BITS>
+__device__ __forceinline__ void store_lane_codes(void* packed, int64_t out_u4, const int (&q)[32]) {
+  u32x4* dst = static_cast<u32x4*>(packed) + out_u4;
+  if constexpr (BITS == 4) {
+    u32x4 w = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) word |= (uint32_t)((q[8 * j + i] + 8) & 15) << (4 * nibble_of(i));
+      w[j] = word;
+    }
+    dst[0] = w;
+  } else {
+    uint32_t words[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        lo |= (uint32_t)(q[8 * j + i] & 0xFF) << (8 * i);
+        hi |= (uint32_t)(q[8 * j + 4 + i] & 0xFF) << (8 * i);
+      }
+      words[2 * j] = lo;
+      words[2 * j + 1] = hi;
+    }
+    dst[0] = u32x4{words[0], words[1], words[2], words[3]};
+    dst[1] = u32x4{words[4], words[5], words[6], words[7]};
+  }
+}
+
+template <int BITS, bool W_BF16, bool S_BF16>
+__global__ __launch_bounds__(256) void pack_to_grid_kernel(const void* __restrict__ W,
+                                                           const uint16_t* __restrict__ scales,
+                                                           void* __restrict__ packed, int K, int N) {
+  LaneCoords c;
+  if (!lane_coords<BITS>(K, N, &c)) return;
+  const float s = scale_to_f32(scales[(int64_t)c.g * N + c.col], S_BF16);
+  const float lo = (BITS == 4) ? -8.0f : -127.0f;
+  const float hi = (BITS == 4) ? 7.0f : 127.0f;
+  int q[32];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int64_t k = c.row0 + 32 * j + i;
+      q[8 * j + i] = quantize_to_grid(load_weight<W_BF16>(W, k * N + c.col), s, lo, hi);
+    }
+  }
+  store_lane_codes<BITS>(packed, c.out_u4, q);
+}
+
+template <int BITS>
+__global__ __launch_bounds__(256) void prepack_kernel(const int8_t* __restrict__ codes,
+                                                      void* __restrict__ packed, int K, int N) {
+  LaneCoords c;
+  if (!lane_coords<BITS>(K, N, &c)) return;
+  int q[32];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[8 * j + i] = codes[(c.row0 + 32 * j + i) * N + c.col];
+  }
+  store_lane_codes<BITS>(packed, c.out_u4, q);
+}
+
+template <int BITS>
+__global__ __launch_bounds__(256) void unpack_kernel(const void* __restrict__ packed,
+                                                     int8_t* __restrict__ codes, int K, int N) {
+  LaneCoords c;
+  if (!lane_coords<BITS>(K, N, &c)) return;
+  const u32x4* src = static_cast<const u32x4*>(packed) + c.out_u4;
+  int q[32];
+  if constexpr (BITS == 4) {
+    const u32x4 w = src[0];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) q[8 * j + i] = (int)((w[j] >> (4 * nibble_of(i))) & 15u) - 8;
+    }
+  } else {
+    const u32x4 a = src[0], b = src[1];
+    const uint32_t words[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) q[8 * j + i] = (int8_t)(words[2 * j + (i >> 2)] >> (8 * (i & 3)));
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) codes[(c.row0 + 32 * j + i) * N + c.col] = (int8_t)q[8 * j + i];
+  }
+}
+
+dim3 tile_grid(int64_t K, int64_t N) {
+  const int64_t lanes = (K / kGroup) * (N / kTileCols) * 64;
+  return dim3((unsigned)((lanes + 255) / 256));
+}
+
+}  // namespace
+
+hipError_t launch_rtn_scales(int bits, const void* W, bool w_bf16, int64_t K, int64_t N,
+                             void* scales, hipStream_t st) {
+  const dim3 grid((unsigned)((N + 255) / 256), (unsigned)(K / kGroup));
+  auto* s = static_cast<uint16_t*>(scales);
+  if (bits == 4) {
+    if (w_bf16) rtn_scales_kernel<4, true><<<grid, 256, 0, st>>>(W, s, (int)K, (int)N);
+    else        rtn_scales_kernel<4, false><<<grid, 256, 0, st>>>(W, s, (int)K, (int)N);
+  } else {
+    if (w_bf16) rtn_scales_kernel<8, true><<<grid, 256, 0, st>>>(W, s, (int)K, (int)N);
+    else        rtn_scales_kernel<8, false><<<grid, 256, 0, st>>>(W, s, (int)K, (int)N);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_to_grid(int bits, const void* W, bool w_bf16, const void* scales,
+                               bool s_bf16, int64_t K, int64_t N, void* packed, hipStream_t st) {
+  const dim3 grid = tile_grid(K, N);
+  const auto* s = static_cast<const uint16_t*>(scales);
+  const int k = (int)K, n = (int)N;
+#define QG_PACK(B, WB, SB) pack_to_grid_kernel<B, WB, SB><<<grid, 256, 0, st>>>(W, s, packed, k, n)
+  if (bits == 4) {
+    if (w_bf16) { if (s_bf16) QG_PACK(4, true, true);  else QG_PACK(4, true, false); }
+    else        { if (s_bf16) QG_PACK(4, false, true); else QG_PACK(4, false, false); }
+  } else {
+    if (w_bf16) { if (s_bf16) QG_PACK(8, true, true);  else QG_PACK(8, true, false); }
+    else        { if (s_bf16) QG_PACK(8, false, true); else QG_PACK(8, false, false); }
+  }
+#undef QG_PACK
+  return hipGetLastError();
+}
+
+hipError_t launch_prepack(int bits, const int8_t* codes, int64_t K, int64_t N, void* packed,
+                          hipStream_t st) {
+  const dim3 grid = tile_grid(K, N);
+  if (bits == 4) prepack_kernel<4><<<grid, 256, 0, st>>>(codes, packed, (int)K, (int)N);
+  else           prepack_kernel<8><<<grid, 256, 0, st>>>(codes, packed, (int)K, (int)N);
+  return hipGetLastError();
+}
+
+hipError_t launch_unpack(int bits, const void* packed, int64_t K, int64_t N, int8_t* codes,
+                         hipStream_t st) {
+  const dim3 grid = tile_grid(K, N);
+  if (bits == 4) unpack_kernel<4><<<grid, 256, 0, st>>>(packed, codes, (int)K, (int)N);
+  else           unpack_kernel<8><<<grid, 256, 0, st>>>(packed, codes, (int)K, (int)N);
+  return hipGetLastError();
+}
+
+}  // namespace qg

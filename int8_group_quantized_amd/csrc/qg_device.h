@@ -1,0 +1,93 @@
+// Device-side helpers shared by the gfx950 kernels: vector types, 16-bit
+// float conversions, and the register-level expansion of packed codes into
+// exact bf16 integers (dequantization with the scale left for later, so every
+// product of an activation and a code is exact).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qg {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+
+constexpr int kGroup = 128;       // K extent of one scale group
+constexpr int kTileCols = 16;     // output columns per packed tile
+constexpr uint32_t kCounterBytes = 65536;  // arrival counters at workspace start
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
+  return __uint_as_float(b << 16);
+}
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t b) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+}
+
+__device__ __forceinline__ float scale_to_f32(uint32_t b, bool s_bf16) {
+  return s_bf16 ? bf16_bits_to_f32(b) : f16_bits_to_f32(b);
+}
+
+// fp32 -> bf16 / fp16 with round-to-nearest-even (the hardware default mode).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+// Fixed-grid quantizer for one weight: clamp(rne(w / s), lo, hi) with IEEE
+// division; s == 0 and NaN quotients give 0, infinite quotients saturate.
+__device__ __forceinline__ int quantize_to_grid(float w, float s, float lo, float hi) {
+  if (s == 0.0f) return 0;
+  const float t = w / s;
+  if (t != t) return 0;
+  return (int)fminf(fmaxf(__builtin_rintf(t), lo), hi);
+}
+
+// One 32-bit word of INT4 codes (eight offset-binary nibbles, nibble p at bits
+// 4p, holding elements i = p/2 + 4*(p%2) ... i.e. nibbles 0..3 are the even
+// elements and 4..7 the odd ones) -> eight bf16 values 128 + u, element order.
+// OR-ing a nibble into the mantissa of 128.0 (0x4300) gives 128 + u exactly;
+// the constant offset 136 = 128 + 8 is removed after the product (see the
+// GEMM kernels), which keeps this expansion at one or two ALU ops per pair.
+__device__ __forceinline__ bf16x8 int4_word_to_biased_bf16(uint32_t w) {
+  u32x4 r;
+  r[0] = (w & 0x000F000Fu) | 0x43004300u;
+  r[1] = ((w >> 4) & 0x000F000Fu) | 0x43004300u;
+  r[2] = ((w >> 8) & 0x000F000Fu) | 0x43004300u;
+  r[3] = ((w >> 12) & 0x000F000Fu) | 0x43004300u;
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// The bias 136 = 128 + 8 in all eight lanes of a B operand (bf16 0x4308).
+__device__ __forceinline__ bf16x8 bias136_bf16x8() {
+  u32x4 r = {0x43084308u, 0x43084308u, 0x43084308u, 0x43084308u};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// Two 32-bit words of INT8 codes (bytes = elements 0..7, two's complement)
+// -> eight exact bf16 integers. Each byte is sign-extended and converted in
+// one instruction; pairs are packed with the bf16 convert (exact: |q| <= 128).
+__device__ __forceinline__ bf16x8 int8_words_to_bf16(uint32_t lo, uint32_t hi) {
+  bf16x8 r;
+  r[0] = (__bf16)(float)(int8_t)(lo);
+  r[1] = (__bf16)(float)(int8_t)(lo >> 8);
+  r[2] = (__bf16)(float)(int8_t)(lo >> 16);
+  r[3] = (__bf16)(float)(int8_t)(lo >> 24);
+  r[4] = (__bf16)(float)(int8_t)(hi);
+  r[5] = (__bf16)(float)(int8_t)(hi >> 8);
+  r[6] = (__bf16)(float)(int8_t)(hi >> 16);
+  r[7] = (__bf16)(float)(int8_t)(hi >> 24);
+  return r;
+}
+
+__device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+}  // namespace qg

@@ -1,0 +1,44 @@
+// Host-side launchers behind the C ABI (one per kernel family). Arguments
+// are already validated by the ABI layer when these are called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "qgemm.h"
+
+namespace qg {
+
+// Small-M tiling: each wavefront covers `nbw` 16-column blocks; `wk`
+// wavefronts of a 4-wave workgroup split the K range of the workgroup;
+// `splits` workgroups split K across the grid (fp32 partials + a last-arrival
+// reduction). Rows are covered 16 at a time (grid z).
+struct SmallPlan {
+  int nbw = 1;
+  int wk = 1;
+  int splits = 1;
+  int gps = 1;        // scale groups per split
+  int wgs_n = 1;      // workgroups along N
+  int row_blocks = 1; // 16-row blocks along M
+};
+
+bool make_small_plan(int bits, int64_t M, int64_t K, int64_t N, int nbw, int wk,
+                     int splits, SmallPlan* plan);
+size_t small_plan_workspace(const SmallPlan& p, int64_t M, int64_t N);
+
+hipError_t launch_rtn_scales(int bits, const void* W, bool w_bf16, int64_t K,
+                             int64_t N, void* scales, hipStream_t st);
+hipError_t launch_pack_to_grid(int bits, const void* W, bool w_bf16,
+                               const void* scales, bool s_bf16, int64_t K,
+                               int64_t N, void* packed, hipStream_t st);
+hipError_t launch_prepack(int bits, const int8_t* codes, int64_t K, int64_t N,
+                          void* packed, hipStream_t st);
+hipError_t launch_unpack(int bits, const void* packed, int64_t K, int64_t N,
+                         int8_t* codes, hipStream_t st);
+hipError_t launch_gemm_small(int bits, const SmallPlan& p, const void* x,
+                             const void* packed, const void* scales, bool s_bf16,
+                             void* out, int64_t M, int64_t K, int64_t N,
+                             void* workspace, hipStream_t st);
+
+}  // namespace qg

@@ -1,0 +1,119 @@
+"""The C-ABI library loads, exports every symbol include/qgemm.h declares, and
+rejects bad arguments on the host with the documented status codes.
+
+No call here reaches the GPU: every case fails validation, which the library
+performs before any HIP call. Pointers are fake but aligned addresses that are
+never dereferenced.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import int8_group_quantized_amd as q
+from int8_group_quantized_amd import binding as b
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qgemm.h")
+
+OK, NULL, SHAPE, ALIGN, DTYPE, WS, HIP, PLAN = range(8)
+FAKE = 0x10000          # aligned, never dereferenced
+MIS = 0x10008           # 8-byte aligned only
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:qg_status|size_t|const char\*)\s+(\w+)\(", text, re.M)))
+
+
+def test_library_exists_and_loads():
+    assert os.path.exists(q.library_path()), "build the library first"
+    assert q.lib() is not None
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 17
+    L = ctypes.CDLL(q.library_path())
+    for n in names:
+        assert hasattr(L, n), n
+    # and the binding describes every one of them
+    assert set(names) == set(b._SIGNATURES)
+
+
+def test_status_strings():
+    L = q.lib()
+    for code in range(8):
+        assert L.qg_status_str(code).decode().startswith(b.STATUS[code])
+
+
+def test_sizes():
+    L = q.lib()
+    assert L.qg_packed_bytes(4, 2560, 19456) == 24903680
+    assert L.qg_packed_bytes(8, 2560, 19456) == 49807360
+    assert L.qg_packed_bytes(4, 100, 16) == 0
+    assert L.qg_packed_bytes(3, 128, 16) == 0
+    assert L.qg_scale_bytes(9728, 2560) == 76 * 2560 * 2
+    assert L.qg_workspace_bytes(4, 0, 128, 16) == 0
+    # a split-K plan needs the counter block plus fp32 partials
+    ws = L.qg_workspace_bytes_plan(4, 3, 1024, 64, 1, 1, 4)
+    assert ws == 65536 + 4 * 3 * 64 * 4
+    assert L.qg_workspace_bytes_plan(4, 3, 1024, 64, 1, 1, 1) == 0
+    assert L.qg_workspace_bytes_plan(4, 3, 1024, 64, 3, 1, 1) == 0   # bad plan -> 0
+
+
+def _gemm(M=1, K=256, N=512, x=FAKE, w=FAKE, s=FAKE, sdt=1, out=FAKE, ws=0, wsb=0, bits=4):
+    f = q.lib().qgemm_w4a16 if bits == 4 else q.lib().qgemm_w8a16
+    return f(x, w, s, sdt, out, M, K, N, ws, wsb, None)
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 100, 512), (1, 0, 512), (1, 256, 0), (1, 256, 24),
+                                   (-1, 256, 512), (1, 2**21, 16), (2**25, 128, 16),
+                                   (70000, 32768, 16)])
+def test_gemm_bad_shapes(M, K, N):
+    assert _gemm(M=M, K=K, N=N) == SHAPE
+    assert _gemm(M=M, K=K, N=N, bits=8) == SHAPE
+
+
+def test_gemm_bad_pointers_and_dtypes():
+    assert _gemm(w=0) == NULL
+    assert _gemm(s=0) == NULL
+    assert _gemm(x=0) == NULL
+    assert _gemm(out=0) == NULL
+    assert _gemm(w=MIS) == ALIGN
+    assert _gemm(x=MIS) == ALIGN
+    assert _gemm(out=MIS + 2) == ALIGN
+    assert _gemm(sdt=2) == DTYPE
+    assert _gemm(sdt=7) == DTYPE
+    # M == 0 is a valid empty call that enqueues nothing
+    assert _gemm(M=0, x=0, out=0) == OK
+
+
+def test_gemm_workspace_rules():
+    L = q.lib()
+    need = L.qg_workspace_bytes_plan(4, 1, 1024, 64, 1, 1, 4)
+    f = L.qgemm_w4a16_plan
+    assert f(FAKE, FAKE, FAKE, 1, FAKE, 1, 1024, 64, 0, 0, 1, 1, 4, None) == WS
+    assert f(FAKE, FAKE, FAKE, 1, FAKE, 1, 1024, 64, FAKE, need - 1, 1, 1, 4, None) == WS
+    assert f(FAKE, FAKE, FAKE, 1, FAKE, 1, 1024, 64, MIS, need, 1, 1, 4, None) == ALIGN
+    assert f(FAKE, FAKE, FAKE, 1, FAKE, 1, 1024, 64, 0, 0, 3, 1, 1, None) == PLAN
+    assert f(FAKE, FAKE, FAKE, 1, FAKE, 1, 1024, 64, 0, 0, 1, 3, 1, None) == PLAN
+    assert f(FAKE, FAKE, FAKE, 1, FAKE, 1, 1024, 64, 0, 0, 1, 1, 9, None) == PLAN
+
+
+def test_pack_entry_points_validate():
+    L = q.lib()
+    assert L.qg_pack_to_grid_w4(FAKE, 2, FAKE, 1, 100, 16, FAKE, None) == SHAPE
+    assert L.qg_pack_to_grid_w4(FAKE, 1, FAKE, 1, 128, 16, FAKE, None) == DTYPE   # fp16 W
+    assert L.qg_pack_to_grid_w8(FAKE, 2, FAKE, 2, 128, 16, FAKE, None) == DTYPE   # fp32 scales
+    assert L.qg_pack_to_grid_w8(FAKE, 2, 0, 0, 128, 16, FAKE, None) == NULL
+    assert L.qg_pack_to_grid_w8(FAKE, 2, FAKE, 0, 128, 16, MIS, None) == ALIGN
+    assert L.qg_rtn_scales_w4(FAKE, 1, 128, 16, FAKE, None) == DTYPE
+    assert L.qg_rtn_scales_w8(0, 2, 128, 16, FAKE, None) == NULL
+    assert L.qg_rtn_scales_w8(FAKE, 2, 128, 8, FAKE, None) == SHAPE
+    for fn in (L.qg_prepack_w4, L.qg_prepack_w8, L.qg_unpack_w4, L.qg_unpack_w8):
+        assert fn(FAKE, 96, 16, FAKE, None) == SHAPE
+        assert fn(0, 128, 16, FAKE, None) == NULL
+        assert fn(FAKE, 128, 16, MIS, None) == ALIGN
