@@ -1,0 +1,301 @@
+"""Benchmark of the group-quantized GEMM path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+
+A step is one decode pass of the hidden-2560 MLP pair at M = 1 (the fused
+gate/up projection K=2560 -> N=19456, then the down projection K=9728 ->
+N=2560), both W4A16 with group-128 INT4 codes and fp16 scales, weights and
+activations already resident in HBM. The reported value is achieved HBM
+throughput on the algorithmic bytes of the step (codes + scales + x + out).
+
+Weights rotate over enough distinct copies (>= 2 x 256 MiB per shape) that
+the 256 MB Infinity Cache cannot serve them, so every step reads HBM. Steps
+are captured in HIP graphs (torch.cuda.graph), so the timing measures the GPU
+rather than Python launch overhead.
+
+Besides the headline line, the same JSON object carries
+  roofline      the dominant kernel (gate/up GEMV), timed live with events;
+  cpu_baseline  the CPU oracle timed on a bounded sample of the same step;
+  workloads     the other shapes (M=16 verification, W8A16 drafter, M=8192
+                prefill, Q_s packing), each with its roofline fraction.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("W4A16 GEMM achieved HBM GB/s (M=1,16) and TFLOP/s (M=8192) vs MI355X roofline")
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix, published
+MALL_BYTES = 256 * 2**20
+GRAPH_CHUNK = 20               # steps per captured graph
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--only-headline", action="store_true", help="skip the other workloads")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def alg_bytes(bits, M, K, N):
+    codes = K * N * bits // 8
+    scales = (K // 128) * N * 2
+    return codes + scales + M * K * 2 + M * N * 2
+
+
+class Weights:
+    """Distinct device copies of one packed weight (RTN on the GPU)."""
+
+    def __init__(self, q, torch, cfg, shape_index, copies):
+        import workloads
+        w = workloads.WORKLOADS[cfg]
+        self.bits, self.M = w["bits"], w["M"]
+        self.K, self.N = w["shapes"][shape_index]
+        W = workloads.weights(self.K, self.N, workloads.seed_for(cfg, shape_index, 0))
+        Wd = torch.from_numpy(W).cuda()
+        s = q.rtn_scales(Wd, self.bits)
+        p = q.pack_to_grid(Wd, s, self.bits)
+        self.W = Wd
+        self.copies = copies
+        self.packed = [p] + [p.clone() for _ in range(copies - 1)]
+        self.scales = [s] + [s.clone() for _ in range(copies - 1)]
+        xb = workloads.activations(self.M, self.K, workloads.seed_for(cfg, shape_index, 1))
+        self.x = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).cuda()
+        self.out = torch.empty((self.M, self.N), dtype=torch.bfloat16, device="cuda")
+        self.ws = torch.zeros(max(q.workspace_bytes(self.bits, self.M, self.K, self.N), 1 << 16),
+                              dtype=torch.uint8, device="cuda")
+        self.bytes = alg_bytes(self.bits, self.M, self.K, self.N)
+        self.flops = 2 * self.M * self.K * self.N
+
+    def call(self, q, i):
+        j = i % len(self.packed)
+        q.qgemm(self.x, self.packed[j], self.scales[j], self.bits, self.N, out=self.out, ws=self.ws)
+
+    def free(self):
+        self.W = None
+        self.packed = self.scales = None
+
+
+def copies_for(bits, K, N):
+    per = K * N * bits // 8 + (K // 128) * N * 2
+    return max(1, math.ceil(2 * MALL_BYTES / per))
+
+
+def capture(torch, fn, n):
+    """A HIP graph of n calls fn(0..n-1) on a capture stream."""
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn_range = list(range(n))
+        for i in fn_range:        # warm the stream once outside capture
+            fn(i)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            for i in fn_range:
+                fn(i)
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graphs(torch, graphs, reps=1):
+    """Milliseconds to replay the list of graphs `reps` times (events on the
+    replay stream, synchronised on both sides)."""
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        for g in graphs:
+            g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1)
+
+
+def graphs_for_steps(torch, step, steps):
+    full, rem = divmod(steps, GRAPH_CHUNK)
+    gs = []
+    if full:
+        g = capture(torch, step, GRAPH_CHUNK)
+        gs += [g] * full
+    if rem:
+        gs.append(capture(torch, step, rem))
+    return gs
+
+
+def kernel_average(torch, wt, q, launches=400):
+    """Average duration of one GEMM launch: a graph of back-to-back launches
+    on rotating weight copies, timed with events."""
+    g = capture(torch, lambda i: wt.call(q, i), 100)
+    for _ in range(2):
+        g.replay()
+    ms = time_graphs(torch, [g], reps=launches // 100)
+    return ms / (100 * (launches // 100))
+
+
+def measure_workload(torch, q, cfg, reps=300):
+    import workloads
+    w = workloads.WORKLOADS[cfg]
+    rows = []
+    for si, (K, N) in enumerate(w["shapes"]):
+        prefill = w["M"] > 16
+        copies = 1 if prefill else copies_for(w["bits"], K, N)
+        wt = Weights(q, torch, cfg, si, copies)
+        wt.W = None
+        n = 4 if prefill else 100
+        g = capture(torch, lambda i: wt.call(q, i), n)
+        g.replay()
+        r = max(1, (20 if prefill else reps) // n)
+        ms = time_graphs(torch, [g], reps=r) / (n * r)
+        row = {"shape": workloads.SHAPE_NAMES.get((K, N), "%dx%d" % (K, N)), "M": w["M"],
+               "K": K, "N": N, "bits": w["bits"], "us_per_call": round(ms * 1e3, 3)}
+        if prefill:
+            tf = wt.flops / (ms * 1e-3) / 1e12
+            row.update(tflops=round(tf, 1), frac_bf16_peak=round(tf / BF16_PEAK_TFLOPS, 4))
+        else:
+            gbs = wt.bytes / (ms * 1e-3) / 1e9
+            row.update(gbs=round(gbs, 1), frac_hbm_peak=round(gbs / HBM_PEAK_GBS, 4),
+                       weight_copies=copies)
+        rows.append(row)
+        wt.free()
+        del g
+        torch.cuda.empty_cache()
+    return {"workload": w["name"], "shapes": rows}
+
+
+def measure_pack(torch, q):
+    """Q_s packing of the gate/up weight (fp32 W in, INT4 tiles out)."""
+    import workloads
+    K, N = 2560, 19456
+    W = torch.from_numpy(workloads.weights(K, N, workloads.seed_for(3, 0, 0))).cuda()
+    s = q.rtn_scales(W, 4)
+    for _ in range(3):
+        q.pack_to_grid(W, s, 4)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    n = 20
+    for _ in range(n):
+        q.pack_to_grid(W, s, 4)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    nbytes = K * N * 4 + (K // 128) * N * 2 + K * N // 2
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": "pack_to_grid_w4 fp32 W", "K": K, "N": N, "us_per_call": round(ms * 1e3, 2),
+            "gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+def cpu_baseline(seconds):
+    """The oracle's product for the headline step, timed on the host."""
+    from oracle import gemm, numerics, quant
+    import workloads
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    cases = []
+    nbytes = 0
+    for si, (K, N) in enumerate(workloads.WORKLOADS[2]["shapes"]):
+        W = workloads.weights(K, N, workloads.seed_for(2, si, 0))
+        sb = quant.rtn_scales(W, 4)
+        codes = quant.q_s(W, numerics.scale_bits_to_f64(sb, "f16"), 4)
+        x = workloads.activations(1, K, workloads.seed_for(2, si, 1))
+        cases.append((x, codes, sb))
+        nbytes += alg_bytes(4, 1, K, N)
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        for x, codes, sb in cases:
+            gemm.gemm_ref(x, codes, sb, "f16")
+        n += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(nbytes * n / dt / 1e9, 3), "unit": "GB/s", "cores": blas_threads,
+            "kind": "oracle",
+            "sample": "%d full decode steps (gate/up 2560x19456 + down 9728x2560, M=1): "
+                      "float64 dequantization + float64 matmul, %.1f s; host has %d CPUs"
+                      % (n, dt, os.cpu_count() or 0)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the path has no multi-GPU step here "
+              "(column or K splits across GPUs are described in the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import int8_group_quantized_amd as q
+    q.lib()
+    torch.cuda.init()
+
+    up = Weights(q, torch, 2, 0, copies_for(4, 2560, 19456))
+    down = Weights(q, torch, 2, 1, copies_for(4, 9728, 2560))
+    up.W = down.W = None
+    torch.cuda.empty_cache()
+
+    def step(i):
+        up.call(q, i)
+        down.call(q, i)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    graphs = graphs_for_steps(torch, step, args.steps)
+    for g in set(graphs):
+        g.replay()
+    ms = time_graphs(torch, graphs) / args.steps
+    step_bytes = up.bytes + down.bytes
+    value = step_bytes / (ms * 1e-3) / 1e9
+
+    k_ms = kernel_average(torch, up, q)
+    k_gbs = up.bytes / (k_ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(k_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(k_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "gemm_small_kernel<4,...> gate/up K=2560 N=19456 M=1",
+                "us_per_launch": round(k_ms * 1e3, 3), "bytes_per_launch": up.bytes}
+    del graphs
+    up.free()
+    down.free()
+    torch.cuda.empty_cache()
+
+    extra = []
+    if not args.only_headline:
+        for cfg in (3, 4, 5):
+            extra.append(measure_workload(torch, q, cfg))
+        extra.append(measure_pack(torch, q))
+
+    cpu = None if args.no_cpu else cpu_baseline(args.cpu_seconds)
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.02) weights -> RTN INT4, N(0,1) bf16 activations)",
+        "config": {"workload": "decode_w4a16_m1: gate/up K=2560 N=19456 + down K=9728 N=2560, "
+                               "M=1, group 128, fp16 scales",
+                   "weight_copies": [up.copies, down.copies],
+                   "bytes_per_step": step_bytes},
+        "roofline": roofline, "cpu_baseline": cpu, "workloads": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

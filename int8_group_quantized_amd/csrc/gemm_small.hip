@@ -5,29 +5,40 @@
 // model card.)
 //
 // The path is HBM-bound: 0.5 (INT4) or 1 (INT8) byte per weight streams once
-// from memory. Each wavefront owns `NBW` 16-column blocks and a slice of the
-// K groups. Per group it
-//   1. loads its packed tile(s) with one 16-byte load per lane per 1 KiB
-//      (fully coalesced: a tile is 1 KiB contiguous, lane l reads bytes
-//      16l..16l+15),
-//   2. loads the matching 16 x 128 slice of x (bf16, L2-resident),
-//   3. expands codes in registers to exact bf16 integers and runs four
-//      16x16x32 bf16 matrix-core ops, giving the group's fp32 partial sums
-//      for 16 rows x 16 columns (rows >= M are zero-filled),
-//   4. multiplies by the group's fp32 scale and adds into the accumulator.
+// from memory. With about one wavefront per SIMD, every vector instruction a
+// wavefront issues costs four cycles of its SIMD, so the kernel is built to
+// keep loads in flight and to spend as few vector instructions per 1 KiB tile
+// as the arithmetic allows:
+//   * a wavefront owns NBW 16-column blocks and a contiguous run of K groups,
+//     walked in batches of D groups held in two register buffers: while one
+//     batch is multiplied the next is being fetched. Each tile is one
+//     16-byte load per lane (a tile is contiguous, so the load is a fully
+//     coalesced 1 KiB transaction) addressed as a wave-uniform base plus a
+//     fixed lane offset; the loop body is straight-line code, so the wait
+//     counters keep a fixed number of loads in flight;
+//   * the workgroup stages its slice of x in LDS with direct global->LDS
+//     loads, in the lane order of the matrix-core A operand, with rows >= M
+//     stored as zeros (MR = 16) or read from a zero block (MR = 1), so each
+//     group is four unconditional 16-byte LDS reads at immediate offsets;
+//   * codes expand in registers to exact bf16 integers (seven ALU ops per
+//     eight INT4 codes, twelve per eight INT8 codes); four 16x16x32 bf16
+//     matrix-core ops give a group's fp32 partial sums for 16 rows x 16
+//     columns, and the group's fp32 scale is applied with one FMA per output.
 // The matrix cores carry the contraction because the vector ALUs cannot: at
 // M = 16 the path needs ~1.8e14 multiply-adds/s to keep pace with HBM, twice
-// the fp32 vector peak, while the 16-row matrix op matches M = 16 exactly.
+// the fp32 vector peak, and the 16-row matrix op fits M = 16 exactly; M = 1
+// uses the same op with one live row (its cost hides under the loads).
 //
 // INT4 codes expand as 128 + u with u = q + 8 (one AND-OR per pair). The bias
 // 136 * sum_k x[m, k] is the same 16x16x32 product with every code equal to
-// 136, evaluated in the same order; subtracting it gives sum x*q. A column
-// whose codes are all zero yields bit-identical sums on both sides, so it
-// comes out exactly 0.
+// 136, evaluated with the same instruction and operand order as the code
+// product, so a column whose codes are all zero cancels to exactly 0.
 //
-// Reductions are deterministic: `WK` wavefronts of a workgroup that split K
-// are summed through LDS in wave order; `splits` workgroups along K write
-// fp32 partials, and whichever arrives last sums them in split order.
+// Reductions are deterministic: WK wavefronts of a workgroup that split K are
+// summed through LDS in wave order; `splits` workgroups along K publish fp32
+// partials with device-coherent stores, count arrivals with one atomic, and
+// the last to arrive sums the partials in split order (no whole-cache flush
+// or invalidate is needed: the partials never sit in a non-coherent cache).
 #include "qg_device.h"
 #include "qg_internal.h"
 
@@ -35,17 +46,68 @@ namespace qg {
 namespace {
 
 constexpr int kMaxCounters = kCounterBytes / sizeof(uint32_t);
+constexpr int64_t kLdsBudget = 80 * 1024;   // dynamic LDS per workgroup (two per CU)
 
-template <int BITS, int NBW, int WK, int U>
-__global__ __launch_bounds__(256) void gemm_small_kernel(
-    const uint16_t* __restrict__ x, const u32x4* __restrict__ packed,
-    const uint16_t* __restrict__ scales, int s_bf16, uint16_t* __restrict__ out,
+// Device-coherent (agent scope) accesses for the split-K partials.
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// INT4 word (nibble p holds element p/2 + 4*(p%2), value q + 8) -> eight
+// bf16 values 128 + u in element order: (w >> 4i) & 0x000F000F | magic per
+// pair. `magic` must arrive as an opaque vector-register value (see
+// opaque_magic) so the compiler selects one AND-OR per pair: a three-operand
+// vector op may read only one scalar or constant operand, and the mask takes
+// that slot.
+__device__ __forceinline__ bf16x8 int4_word_to_biased(uint32_t w, uint32_t magic) {
+  const u32x4 r = {(w & 0x000F000Fu) | magic, ((w >> 4) & 0x000F000Fu) | magic,
+                   ((w >> 8) & 0x000F000Fu) | magic, ((w >> 12) & 0x000F000Fu) | magic};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// 0x43004300 (two bf16 128.0) held in a vector register the optimiser
+// cannot fold back into a literal. The empty asm emits no instruction.
+__device__ __forceinline__ uint32_t opaque_magic() {
+  uint32_t m = 0x43004300u;
+  asm volatile("" : "+v"(m));
+  return m;
+}
+
+template <int BITS>
+struct Tile {
+  static constexpr int bytes = (BITS == 4) ? 1024 : 2048;
+  static constexpr int words = bytes / 1024;   // 16-byte words per lane
+};
+
+// Groups per batch: two batches of D x NBW tiles stay in registers, and a
+// batch's tiles of one column block sit within the 4 KiB immediate-offset
+// reach of a load instruction.
+template <int BITS, int NBW>
+struct Batch {
+  static constexpr int D = (BITS == 4) ? (NBW == 1 ? 4 : (NBW == 2 ? 2 : 1))
+                                       : (NBW == 1 ? 2 : 1);
+};
+
+template <int BITS, bool SBF, int MR, int NBW, int WN, int WK>
+__global__ __launch_bounds__(64 * WN * WK, 2) void gemm_small_kernel(
+    const uint16_t* __restrict__ x, const char* __restrict__ packed,
+    const uint16_t* __restrict__ scales, uint16_t* __restrict__ out,
     uint32_t* __restrict__ counters, float* __restrict__ partials, int M, int K, int N,
-    int splits, int gps) {
-  constexpr int WN = 4 / WK;                 // wavefronts along N in a workgroup
-  constexpr int TU4 = (BITS == 4) ? 1 : 2;   // 16-byte words per lane per tile
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+    int splits, int gps, int sg) {
+  constexpr int NT = 64 * WN * WK;
+  constexpr int NW = WN * WK;
+  constexpr int TB = Tile<BITS>::bytes;
+  constexpr int TW = Tile<BITS>::words;
+  constexpr int D = Batch<BITS, NBW>::D;
+  constexpr int XG = (MR == 1) ? 16 : 256;   // LDS 16-byte words of x per group
+  extern __shared__ u32x4 smem[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wn = wave % WN;
   const int wk = wave / WN;
   const int G = K >> 7;
@@ -54,49 +116,64 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(
   const int nvalid = min(NBW, NB - cb0);     // column blocks this wave owns (may be <= 0)
   const int split = blockIdx.y;
   const int row0 = blockIdx.z * 16;
-  const int g_end = min(G, (split + 1) * gps);
+  const int mrows = min(16, M - row0);       // live rows in this 16-row block
+  const int wg_g0 = split * gps;             // first group of the workgroup
+  const int wg_gn = min(G, wg_g0 + gps) - wg_g0;
   const int l16 = lane & 15;                 // A row / C column of this lane
   const int lq = lane >> 4;                  // K slice (A, B) / row quad (C)
-  const bool row_ok = row0 + l16 < M;
-  const uint16_t* xrow = x + (int64_t)(row0 + l16) * K + 8 * lq;
-  const bool sbf = s_bf16 != 0;
+  u32x4* xs = smem;                          // [sg][XG] x fragments, then a zero block
+  const uint32_t magic = opaque_magic();
+
+  int cb[NBW];
+#pragma unroll
+  for (int c = 0; c < NBW; ++c) cb[c] = min(cb0 + c, NB - 1);   // clamped: loads stay in range
+  const int lane_off = lane * (TB / 64);
+  // x fragment address of this lane for stage group 0, and its per-group step
+  // (in 16-byte words); with MR == 1 only lanes of row 0 read data, the rest
+  // read the zero block.
+  const int xa_lane = (MR == 1) ? ((l16 == 0) ? lq : sg * XG) : lane;
+  const int xa_step = (MR == 1) ? ((l16 == 0) ? XG : 0) : XG;
 
   f32x4 acc[NBW];
 #pragma unroll
   for (int c = 0; c < NBW; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  if (nvalid > 0) {
-    for (int g0 = split * gps + wk; g0 < g_end; g0 += U * WK) {
-      u32x4 xa[U][4];
-      u32x4 wt[U][NBW][TU4];
-      float sc[U][NBW];
-      // Issue every load of the chunk before any arithmetic.
+  for (int s0 = 0; s0 < wg_gn; s0 += sg) {
+    const int sn = min(sg, wg_gn - s0);
+    const int per = (sn + WK - 1) / WK;
+    const int w_lo = min(sn, wk * per);
+    const int w_n = min(sn, w_lo + per) - w_lo;   // may be 0 for trailing waves
+    const int g_first = wg_g0 + s0 + w_lo;
+    const int g_last = wg_g0 + s0 + max(w_lo + w_n - 1, 0);
+    const int nbatch = (w_n + D - 1) / D;
+
+    u32x4 ta[D][NBW][TW], tb[D][NBW][TW];
+    uint32_t sa[D][NBW], sb[D][NBW];
+    // Batch b: groups g_first + b*D + d, clamped to g_last (extra ones are
+    // recomputed and weighted by zero).
+    auto load_batch = [&](int b, u32x4 (&t)[D][NBW][TW], uint32_t (&s)[D][NBW]) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int g = g0 + u * WK;
-        if (g < g_end) {
+      for (int d = 0; d < D; ++d) {
+        const int g = min(g_first + b * D + d, g_last);
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            xa[u][j] = row_ok ? *reinterpret_cast<const u32x4*>(xrow + (int64_t)g * 128 + 32 * j)
-                              : u32x4{0u, 0u, 0u, 0u};
+        for (int c = 0; c < NBW; ++c) {
+          const char* tp = packed + ((int64_t)cb[c] * G + g) * TB + lane_off;
 #pragma unroll
-          for (int c = 0; c < NBW; ++c) {
-            if (c < nvalid) {
-              const int64_t t = (int64_t)(cb0 + c) * G + g;
-#pragma unroll
-              for (int v = 0; v < TU4; ++v) wt[u][c][v] = packed[(t * 64 + lane) * TU4 + v];
-              sc[u][c] = scale_to_f32(scales[(int64_t)g * N + (cb0 + c) * 16 + l16], sbf);
-            }
-          }
+          for (int v = 0; v < TW; ++v) t[d][c][v] = *reinterpret_cast<const u32x4*>(tp + 16 * v);
+          s[d][c] = scales[(int64_t)g * N + cb[c] * 16 + l16];
         }
       }
+    };
+    auto compute_batch = [&](int b, const u32x4 (&t)[D][NBW][TW], const uint32_t (&s)[D][NBW]) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int g = g0 + u * WK;
-        if (g >= g_end) break;
+      for (int d = 0; d < D; ++d) {
+        const int i = b * D + d;                      // wave-relative group
+        const bool live = i < w_n;
+        const int gl = w_lo + min(i, w_n - 1);        // stage-relative group
+        const u32x4* xp = xs + xa_lane + gl * xa_step;
         bf16x8 a[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) a[j] = __builtin_bit_cast(bf16x8, xa[u][j]);
+        for (int j = 0; j < 4; ++j) a[j] = __builtin_bit_cast(bf16x8, xp[j * (XG / 4)]);
         f32x4 bias = {0.f, 0.f, 0.f, 0.f};
         if constexpr (BITS == 4) {
           const bf16x8 b136 = bias136_bf16x8();
@@ -105,40 +182,93 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(
         }
 #pragma unroll
         for (int c = 0; c < NBW; ++c) {
-          if (c < nvalid) {
-            f32x4 p = {0.f, 0.f, 0.f, 0.f};
-            if constexpr (BITS == 4) {
+          f32x4 p = {0.f, 0.f, 0.f, 0.f};
+          if constexpr (BITS == 4) {
 #pragma unroll
-              for (int j = 0; j < 4; ++j)
-                p = mfma16x16x32(a[j], int4_word_to_biased_bf16(wt[u][c][0][j]), p);
-            } else {
-              p = mfma16x16x32(a[0], int8_words_to_bf16(wt[u][c][0][0], wt[u][c][0][1]), p);
-              p = mfma16x16x32(a[1], int8_words_to_bf16(wt[u][c][0][2], wt[u][c][0][3]), p);
-              p = mfma16x16x32(a[2], int8_words_to_bf16(wt[u][c][1][0], wt[u][c][1][1]), p);
-              p = mfma16x16x32(a[3], int8_words_to_bf16(wt[u][c][1][2], wt[u][c][1][3]), p);
-            }
+            for (int j = 0; j < 4; ++j)
+              p = mfma16x16x32(a[j], int4_word_to_biased(t[d][c][0][j], magic), p);
+          } else {
+            p = mfma16x16x32(a[0], int8_words_to_bf16(t[d][c][0][0], t[d][c][0][1]), p);
+            p = mfma16x16x32(a[1], int8_words_to_bf16(t[d][c][0][2], t[d][c][0][3]), p);
+            p = mfma16x16x32(a[2], int8_words_to_bf16(t[d][c][1][0], t[d][c][1][1]), p);
+            p = mfma16x16x32(a[3], int8_words_to_bf16(t[d][c][1][2], t[d][c][1][3]), p);
+          }
+          const float sv = SBF ? bf16_bits_to_f32(s[d][c]) : f16_bits_to_f32(s[d][c]);
+          const float scale = live ? sv : 0.0f;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[c][e] = fmaf(sc[u][c], p[e] - bias[e], acc[c][e]);
+          for (int e = 0; e < 4; ++e) acc[c][e] = fmaf(scale, p[e] - bias[e], acc[c][e]);
+        }
+      }
+    };
+
+    // Both register batches in flight while x is staged.
+    load_batch(0, ta, sa);
+    load_batch(1, tb, sb);
+    if (s0 > 0) __syncthreads();             // every wave is done with the last stage
+    {
+      // Stage x with direct global->LDS loads: one wavefront instruction fills
+      // one contiguous 1 KiB block of the layout (lane l -> 16 bytes at l*16).
+      // Slots of rows >= M are written with zeros by the lanes that skip the
+      // load, so no slot is written twice.
+      const int total = sn * XG;                      // 16-byte words to fill
+      for (int w0 = wave * 64; w0 < total; w0 += NW * 64) {
+        const int e = w0 + lane;
+        int g, j, q, r;
+        if constexpr (MR == 1) {
+          g = e >> 4; j = (e >> 2) & 3; q = e & 3; r = 0;
+        } else {
+          g = e >> 8; j = (e >> 6) & 3; q = (e >> 4) & 3; r = e & 15;
+        }
+        if (e < total) {
+          if (r < mrows) {
+            const uint16_t* src = x + (int64_t)(row0 + r) * K + (int64_t)(wg_g0 + s0 + g) * 128 +
+                                  32 * j + 8 * q;
+            __builtin_amdgcn_global_load_lds(
+                src, (__attribute__((address_space(3))) void*)(xs + w0), 16, 0, 0);
+          } else {
+            xs[e] = u32x4{0u, 0u, 0u, 0u};
           }
         }
       }
+      if constexpr (MR == 1) {
+        if (tid < 16) xs[sg * XG + tid] = u32x4{0u, 0u, 0u, 0u};   // zero block for rows >= 1
+      }
+    }
+    // The direct-to-LDS loads (and, with them, both tile batches) must land
+    // before any wavefront reads the staged x.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+
+    if (w_n > 0) {
+      // Batches in pairs: multiply one while the other is in flight. The loop
+      // body is straight-line code (fetches past the wave's last group are
+      // clamped, redundant and discarded); an odd last batch runs on its own.
+      int b = 0;
+      for (; b + 1 < nbatch; b += 2) {
+        compute_batch(b, ta, sa);
+        load_batch(b + 2, ta, sa);
+        compute_batch(b + 1, tb, sb);
+        load_batch(b + 3, tb, sb);
+      }
+      if (b < nbatch) compute_batch(b, ta, sa);
     }
   }
 
-  // Wavefronts that split K inside the workgroup: reduce through LDS.
+  // Wavefronts that split K inside the workgroup: reduce through LDS (the x
+  // slice is dead by now, so its space is reused after a barrier).
   if constexpr (WK > 1) {
-    __shared__ f32x4 red[WK - 1][WN][NBW][64];
+    __syncthreads();
+    f32x4* red = reinterpret_cast<f32x4*>(smem);       // [WK-1][WN][NBW][64]
     if (wk > 0) {
 #pragma unroll
-      for (int c = 0; c < NBW; ++c) red[wk - 1][wn][c][lane] = acc[c];
+      for (int c = 0; c < NBW; ++c) red[(((wk - 1) * WN + wn) * NBW + c) * 64 + lane] = acc[c];
     }
     __syncthreads();
     if (wk == 0) {
-#pragma unroll
       for (int w = 0; w < WK - 1; ++w) {
 #pragma unroll
         for (int c = 0; c < NBW; ++c) {
-          const f32x4 o = red[w][wn][c][lane];
+          const f32x4 o = red[((w * WN + wn) * NBW + c) * 64 + lane];
 #pragma unroll
           for (int e = 0; e < 4; ++e) acc[c][e] += o[e];
         }
@@ -155,8 +285,8 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(
           const int n = (cb0 + c) * 16 + l16;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int row = row0 + 4 * lq + e;
-            if (row < M) out[(int64_t)row * N + n] = f32_to_bf16_bits(acc[c][e]);
+            const int r = 4 * lq + e;
+            if (r < mrows) out[(int64_t)(row0 + r) * N + n] = f32_to_bf16_bits(acc[c][e]);
           }
         }
       }
@@ -171,25 +301,25 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(
         const int n = (cb0 + c) * 16 + l16;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int row = row0 + 4 * lq + e;
-          if (row < M) partials[((int64_t)split * M + row) * N + n] = acc[c][e];
+          const int r = 4 * lq + e;
+          if (r < mrows)
+            store_coherent(&partials[((int64_t)split * M + row0 + r) * N + n], acc[c][e]);
         }
       }
     }
   }
-  // Publish this workgroup's partials device-wide, then count arrivals.
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  // The coherent stores must have completed before the arrival is counted.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   __shared__ uint32_t s_last;
   const uint32_t cidx = blockIdx.z * gridDim.x + blockIdx.x;
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     const uint32_t prev =
         __hip_atomic_fetch_add(&counters[cidx], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_last = (prev == (uint32_t)splits - 1u) ? 1u : 0u;
   }
   __syncthreads();
   if (s_last == 0u) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   if (wk == 0) {
 #pragma unroll
     for (int c = 0; c < NBW; ++c) {
@@ -197,24 +327,25 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(
         const int n = (cb0 + c) * 16 + l16;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int row = row0 + 4 * lq + e;
-          if (row < M) {
+          const int r = 4 * lq + e;
+          if (r < mrows) {
             float sum = 0.0f;
-            for (int sp = 0; sp < splits; ++sp) sum += partials[((int64_t)sp * M + row) * N + n];
-            out[(int64_t)row * N + n] = f32_to_bf16_bits(sum);
+            for (int sp = 0; sp < splits; ++sp)
+              sum += load_coherent(&partials[((int64_t)sp * M + row0 + r) * N + n]);
+            out[(int64_t)(row0 + r) * N + n] = f32_to_bf16_bits(sum);
           }
         }
       }
     }
   }
-  if (threadIdx.x == 0) counters[cidx] = 0u;   // ready for the next call
+  if (tid == 0)   // ready for the next call on this workspace
+    __hip_atomic_store(&counters[cidx], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int BITS, int NBW, int WK>
+template <int BITS, bool SBF, int MR, int NBW, int WN, int WK>
 hipError_t launch_variant(const SmallPlan& p, const void* x, const void* packed,
-                          const void* scales, bool s_bf16, void* out, int64_t M, int64_t K,
-                          int64_t N, void* ws, hipStream_t st) {
-  constexpr int U = (NBW >= 4) ? 2 : 4;
+                          const void* scales, void* out, int64_t M, int64_t K, int64_t N,
+                          void* ws, hipStream_t st) {
   const dim3 grid((unsigned)p.wgs_n, (unsigned)p.splits, (unsigned)p.row_blocks);
   uint32_t* counters = nullptr;
   float* partials = nullptr;
@@ -222,60 +353,86 @@ hipError_t launch_variant(const SmallPlan& p, const void* x, const void* packed,
     counters = static_cast<uint32_t*>(ws);
     partials = reinterpret_cast<float*>(static_cast<char*>(ws) + kCounterBytes);
   }
-  gemm_small_kernel<BITS, NBW, WK, U><<<grid, 256, 0, st>>>(
-      static_cast<const uint16_t*>(x), static_cast<const u32x4*>(packed),
-      static_cast<const uint16_t*>(scales), s_bf16 ? 1 : 0, static_cast<uint16_t*>(out),
-      counters, partials, (int)M, (int)K, (int)N, p.splits, p.gps);
+  const size_t lds = small_plan_lds_bytes(p, M);
+  gemm_small_kernel<BITS, SBF, MR, NBW, WN, WK><<<grid, 64 * WN * WK, lds, st>>>(
+      static_cast<const uint16_t*>(x), static_cast<const char*>(packed),
+      static_cast<const uint16_t*>(scales), static_cast<uint16_t*>(out), counters, partials,
+      (int)M, (int)K, (int)N, p.splits, p.gps, p.sg);
   return hipGetLastError();
 }
 
-template <int BITS>
-hipError_t launch_bits(const SmallPlan& p, const void* x, const void* packed, const void* scales,
-                       bool s_bf16, void* out, int64_t M, int64_t K, int64_t N, void* ws,
-                       hipStream_t st) {
-#define QG_V(NBW, WK)                                                                       \
-  if (p.nbw == NBW && p.wk == WK)                                                           \
-    return launch_variant<BITS, NBW, WK>(p, x, packed, scales, s_bf16, out, M, K, N, ws, st);
-  QG_V(1, 1) QG_V(1, 2) QG_V(1, 4)
-  QG_V(2, 1) QG_V(2, 2) QG_V(2, 4)
-  QG_V(4, 1) QG_V(4, 2) QG_V(4, 4)
+template <int BITS, bool SBF, int MR>
+hipError_t launch_shape(const SmallPlan& p, const void* x, const void* packed, const void* scales,
+                        void* out, int64_t M, int64_t K, int64_t N, void* ws, hipStream_t st) {
+#define QG_V(NBW, WN, WK)                                                                    \
+  if (p.nbw == NBW && p.wn == WN && p.wk == WK)                                              \
+    return launch_variant<BITS, SBF, MR, NBW, WN, WK>(p, x, packed, scales, out, M, K, N, ws, st);
+  QG_V(1, 4, 1) QG_V(1, 2, 2) QG_V(1, 1, 4) QG_V(1, 1, 8)
+  QG_V(2, 4, 1) QG_V(2, 1, 4)
+  QG_V(4, 4, 1) QG_V(4, 1, 4)
 #undef QG_V
   return hipErrorInvalidValue;
 }
 
+bool shape_supported(int nbw, int wn, int wk) {
+  static const int ok[][3] = {{1, 4, 1}, {1, 2, 2}, {1, 1, 4}, {1, 1, 8},
+                              {2, 4, 1}, {2, 1, 4}, {4, 4, 1}, {4, 1, 4}};
+  for (const auto& s : ok)
+    if (s[0] == nbw && s[1] == wn && s[2] == wk) return true;
+  return false;
+}
+
+// LDS bytes per stage group: x fragments, rows padded to 16 unless M == 1.
+int64_t lds_per_group(int bits, int wn, int mr) {
+  (void)bits;
+  (void)wn;
+  return mr == 1 ? 256 : 4096;
+}
+
 }  // namespace
+
+size_t small_plan_lds_bytes(const SmallPlan& p, int64_t M) {
+  (void)M;
+  const size_t stage = (size_t)p.sg * (size_t)lds_per_group(p.bits, p.wn, p.mr) + 256;
+  const size_t red = (size_t)(p.wk - 1) * p.wn * p.nbw * 64 * 16;
+  return stage > red ? stage : red;
+}
 
 bool make_small_plan(int bits, int64_t M, int64_t K, int64_t N, int nbw, int wk, int splits,
                      SmallPlan* plan) {
-  (void)bits;
   const int64_t NB = N / kTileCols;
   const int64_t G = K / kGroup;
   SmallPlan p;
+  p.bits = bits;
+  p.mr = (M == 1) ? 1 : 16;
   p.row_blocks = (int)((M + 15) / 16);
-  if (nbw == 0) nbw = (M > 16) ? 2 : 1;
-  if (wk == 0) wk = (M > 16) ? 1 : 4;
-  if (nbw != 1 && nbw != 2 && nbw != 4) return false;
-  if (wk != 1 && wk != 2 && wk != 4) return false;
-  const int64_t wn = 4 / wk;
+  if (nbw == 0) nbw = 1;
+  if (wk == 0) {
+    // Enough column-block waves to fill the chip without splitting K, else
+    // waves that split K inside a workgroup.
+    wk = (NB >= 1024) ? 1 : (NB >= 128 ? 4 : 8);
+  }
+  const int wn = (wk >= 8) ? 1 : ((nbw >= 2 && wk == 4) ? 1 : 4 / wk);
+  if (!shape_supported(nbw, wn, wk)) return false;
   p.nbw = nbw;
   p.wk = wk;
-  p.wgs_n = (int)((NB + wn * nbw - 1) / (wn * nbw));
+  p.wn = wn;
+  p.wgs_n = (int)((NB + (int64_t)wn * nbw - 1) / ((int64_t)wn * nbw));
+  const int64_t max_sg = (kLdsBudget - 256) / lds_per_group(bits, wn, p.mr);
   if (splits == 0) {
-    if (M > 16) {
-      splits = 1;
-    } else {
-      // Aim for ~1024 workgroups (4 per compute unit), at least 4 groups each.
-      const int64_t want = (1024 + p.wgs_n - 1) / p.wgs_n;
-      const int64_t cap = G / 4 > 1 ? G / 4 : 1;
-      splits = (int)(want < cap ? want : cap);
-      if (splits < 1) splits = 1;
-    }
+    // Split K across workgroups when one workgroup's x slice would not fit
+    // in LDS (M <= 16 only: beyond that, stages avoid a large workspace).
+    splits = (M <= 16) ? (int)((G + max_sg - 1) / max_sg) : 1;
   }
   if (splits < 1 || splits > G) return false;
   p.gps = (int)((G + splits - 1) / splits);
   p.splits = (int)((G + p.gps - 1) / p.gps);   // no empty split
+  // Stage size: as many groups as fit the LDS budget, balanced across stages.
+  const int64_t stages = (p.gps + max_sg - 1) / max_sg;
+  p.sg = (int)((p.gps + stages - 1) / stages);
   if (p.splits > 65535 || p.row_blocks > 65535) return false;
   if (p.splits > 1 && (int64_t)p.wgs_n * p.row_blocks > kMaxCounters) return false;
+  if ((int64_t)small_plan_lds_bytes(p, M) > kLdsBudget) return false;
   *plan = p;
   return true;
 }
@@ -288,8 +445,13 @@ size_t small_plan_workspace(const SmallPlan& p, int64_t M, int64_t N) {
 hipError_t launch_gemm_small(int bits, const SmallPlan& p, const void* x, const void* packed,
                              const void* scales, bool s_bf16, void* out, int64_t M, int64_t K,
                              int64_t N, void* ws, hipStream_t st) {
-  if (bits == 4) return launch_bits<4>(p, x, packed, scales, s_bf16, out, M, K, N, ws, st);
-  return launch_bits<8>(p, x, packed, scales, s_bf16, out, M, K, N, ws, st);
+#define QG_B(B, S, R)                                                                     \
+  if (bits == B && s_bf16 == S && p.mr == R)                                              \
+    return launch_shape<B, S, R>(p, x, packed, scales, out, M, K, N, ws, st);
+  QG_B(4, false, 1) QG_B(4, false, 16) QG_B(4, true, 1) QG_B(4, true, 16)
+  QG_B(8, false, 1) QG_B(8, false, 16) QG_B(8, true, 1) QG_B(8, true, 16)
+#undef QG_B
+  return hipErrorInvalidValue;
 }
 
 }  // namespace qg

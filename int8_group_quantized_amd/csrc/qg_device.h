@@ -70,20 +70,27 @@ __device__ __forceinline__ bf16x8 bias136_bf16x8() {
   return __builtin_bit_cast(bf16x8, r);
 }
 
+// Sign-extended byte e of w as fp32 (one byte-select convert instruction).
+__device__ __forceinline__ float sbyte_to_f32(uint32_t w, int e) {
+  return (float)((int)(w << (24 - 8 * e)) >> 24);
+}
+
+// Two fp32 values -> one word of two bf16 (RNE; exact for small integers).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+  const bf16x2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 // Two 32-bit words of INT8 codes (bytes = elements 0..7, two's complement)
-// -> eight exact bf16 integers. Each byte is sign-extended and converted in
-// one instruction; pairs are packed with the bf16 convert (exact: |q| <= 128).
+// -> eight exact bf16 integers: eight byte-select converts and four pair
+// packs (exact, |q| <= 128).
 __device__ __forceinline__ bf16x8 int8_words_to_bf16(uint32_t lo, uint32_t hi) {
-  bf16x8 r;
-  r[0] = (__bf16)(float)(int8_t)(lo);
-  r[1] = (__bf16)(float)(int8_t)(lo >> 8);
-  r[2] = (__bf16)(float)(int8_t)(lo >> 16);
-  r[3] = (__bf16)(float)(int8_t)(lo >> 24);
-  r[4] = (__bf16)(float)(int8_t)(hi);
-  r[5] = (__bf16)(float)(int8_t)(hi >> 8);
-  r[6] = (__bf16)(float)(int8_t)(hi >> 16);
-  r[7] = (__bf16)(float)(int8_t)(hi >> 24);
-  return r;
+  const u32x4 r = {pack_bf16x2(sbyte_to_f32(lo, 0), sbyte_to_f32(lo, 1)),
+                   pack_bf16x2(sbyte_to_f32(lo, 2), sbyte_to_f32(lo, 3)),
+                   pack_bf16x2(sbyte_to_f32(hi, 0), sbyte_to_f32(hi, 1)),
+                   pack_bf16x2(sbyte_to_f32(hi, 2), sbyte_to_f32(hi, 3))};
+  return __builtin_bit_cast(bf16x8, r);
 }
 
 __device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, const f32x4& c) {

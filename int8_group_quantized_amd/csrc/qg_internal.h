@@ -15,10 +15,14 @@ namespace qg {
 // `splits` workgroups split K across the grid (fp32 partials + a last-arrival
 // reduction). Rows are covered 16 at a time (grid z).
 struct SmallPlan {
+  int bits = 4;
+  int mr = 16;        // 1: single-row layout of x in LDS; 16: rows padded to 16
   int nbw = 1;
+  int wn = 4;         // wavefronts along N in a workgroup
   int wk = 1;
   int splits = 1;
-  int gps = 1;        // scale groups per split
+  int gps = 1;        // scale groups per split (one workgroup's K range)
+  int sg = 1;         // groups per LDS stage of x
   int wgs_n = 1;      // workgroups along N
   int row_blocks = 1; // 16-row blocks along M
 };
@@ -26,6 +30,7 @@ struct SmallPlan {
 bool make_small_plan(int bits, int64_t M, int64_t K, int64_t N, int nbw, int wk,
                      int splits, SmallPlan* plan);
 size_t small_plan_workspace(const SmallPlan& p, int64_t M, int64_t N);
+size_t small_plan_lds_bytes(const SmallPlan& p, int64_t M);
 
 hipError_t launch_rtn_scales(int bits, const void* W, bool w_bf16, int64_t K,
                              int64_t N, void* scales, hipStream_t st);

@@ -46,7 +46,8 @@ def _assert_close(got, ref, what=""):
                              % (what, (~ok).sum(), ok.size, gemm.rms(ref), detail))
 
 
-PLANS = [None, (1, 1, 1), (1, 4, 1), (2, 2, 3), (4, 1, 2), (4, 4, 5), (1, 2, 7), (2, 4, 2)]
+PLANS = [None, (1, 1, 1), (1, 4, 1), (2, 4, 3), (4, 1, 2), (4, 4, 5), (1, 2, 7), (2, 1, 2),
+         (1, 8, 2)]
 SHAPES = [(1, 256, 512), (3, 896, 592), (16, 1280, 272), (7, 384, 48), (16, 128, 16)]
 
 
@@ -65,8 +66,8 @@ def test_small_shapes_every_plan(bits, M, K, N):
         if plan is not None and plan[2] == 1 and first is None:
             first = got
     # every plan is a valid summation order; repeated calls are bit-identical
-    a = _run(bits, x, c, s, N, (2, 2, min(3, G)))
-    b = _run(bits, x, c, s, N, (2, 2, min(3, G)))
+    a = _run(bits, x, c, s, N, (2, 4, min(3, G)))
+    b = _run(bits, x, c, s, N, (2, 4, min(3, G)))
     assert np.array_equal(a, b)
 
 
@@ -150,7 +151,7 @@ def test_workspace_reuse_across_plans():
     ws = torch.zeros(1 << 20, dtype=torch.uint8, device="cuda:0")
     pg = q.prepack(dev_i8(c), 4)
     xd, sd = dev_bf16(x), dev_scales(s, "f16")
-    for plan in [(1, 1, 10), (2, 2, 3), (1, 1, 10), (4, 4, 2), (1, 1, 1), (2, 1, 5)]:
+    for plan in [(1, 1, 10), (2, 4, 3), (1, 1, 10), (4, 4, 2), (1, 1, 1), (2, 1, 5)]:
         out = q.qgemm_w4a16(xd, pg, sd, N, plan=plan, ws=ws)
         _assert_close(numerics.bf16_to_f64(host_u16(out)), ref, str(plan))
     assert torch.count_nonzero(ws[:65536]) == 0
