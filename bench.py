@@ -47,7 +47,46 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only-headline", action="store_true", help="skip the other workloads")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a 256 MiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_small_w4a16_gate_up_m1.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "int8_group_quantized_amd", "csrc", f)
+                  for f in ("gemm_small.hip", "qg_device.h")]
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed counter summary, or None when
+    the kernel sources changed since the counters were taken."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def copy_calibration(torch):
+    """A plain 256 MiB device-to-device copy of known size: its byte counters
+    scale the GEMM's counter readings to bytes."""
+    n = 256 * 2**20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    for _ in range(3):
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del dst
 
 
 def alg_bytes(bits, M, K, N):
@@ -268,7 +307,7 @@ def main():
     k_ms = kernel_average(torch, up, q)
     k_gbs = up.bytes / (k_ms * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(k_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(k_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(k_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                 "kernel": "gemm_small_kernel<4,...> gate/up K=2560 N=19456 M=1",
                 "us_per_launch": round(k_ms * 1e3, 3), "bytes_per_launch": up.bytes}
     del graphs
@@ -282,6 +321,8 @@ def main():
             extra.append(measure_workload(torch, q, cfg))
         extra.append(measure_pack(torch, q))
 
+    if args.copy_calibration:
+        copy_calibration(torch)
     cpu = None if args.no_cpu else cpu_baseline(args.cpu_seconds)
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,

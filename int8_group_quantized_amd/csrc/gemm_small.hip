@@ -195,8 +195,14 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_small_kernel(
           }
           const float sv = SBF ? bf16_bits_to_f32(s[d][c]) : f16_bits_to_f32(s[d][c]);
           const float scale = live ? sv : 0.0f;
+          if constexpr (MR == 1) {
+            // One live row: only element 0 of the lanes holding rows 0..3 is
+            // ever stored, so the other three rows are not accumulated.
+            acc[c][0] = fmaf(scale, p[0] - bias[0], acc[c][0]);
+          } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc[c][e] = fmaf(scale, p[e] - bias[e], acc[c][e]);
+            for (int e = 0; e < 4; ++e) acc[c][e] = fmaf(scale, p[e] - bias[e], acc[c][e]);
+          }
         }
       }
     };
