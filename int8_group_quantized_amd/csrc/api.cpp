@@ -13,6 +13,7 @@ namespace {
 constexpr int64_t kMaxKN = int64_t(1) << 20;
 constexpr int64_t kMaxM = int64_t(1) << 24;
 constexpr int64_t kMaxElems = int64_t(1) << 31;
+constexpr int64_t kSmallMaxM = 16;   // above this, the library's own plan is the prefill kernel
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -85,6 +86,13 @@ qg_status gemm(int bits, const void* x, const void* packed, const void* scales, 
   if ((s = check_ptrs({packed, scales})) != QG_OK) return s;
   if (M == 0) return QG_OK;
   if ((s = check_ptrs({x, out})) != QG_OK) return s;
+  const bool explicit_plan = (nbw != 0 || wk != 0 || splits != 0);
+  if (M > kSmallMaxM && !explicit_plan) {
+    qg::PrefillPlan pp;
+    if (!qg::make_prefill_plan(M, K, N, &pp)) return QG_ERR_SHAPE;
+    return from_hip(qg::launch_gemm_prefill(bits, pp, x, packed, scales, s_dt == QG_BF16, out,
+                                            M, K, N, as_stream(stream)));
+  }
   qg::SmallPlan plan;
   if (!qg::make_small_plan(bits, M, K, N, nbw, wk, splits, &plan)) return QG_ERR_PLAN;
   const size_t need = qg::small_plan_workspace(plan, M, N);
@@ -98,6 +106,7 @@ qg_status gemm(int bits, const void* x, const void* packed, const void* scales, 
 
 size_t workspace_bytes(int bits, int64_t M, int64_t K, int64_t N, int nbw, int wk, int splits) {
   if ((bits != 4 && bits != 8) || check_mkn(M, K, N) != QG_OK || M == 0) return 0;
+  if (M > kSmallMaxM && nbw == 0 && wk == 0 && splits == 0) return 0;   // prefill kernel
   qg::SmallPlan plan;
   if (!qg::make_small_plan(bits, M, K, N, nbw, wk, splits, &plan)) return 0;
   return qg::small_plan_workspace(plan, M, N);

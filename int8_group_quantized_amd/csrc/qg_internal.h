@@ -27,6 +27,18 @@ struct SmallPlan {
   int row_blocks = 1; // 16-row blocks along M
 };
 
+// Large-M (prefill) tiling: 128 x 128 output tiles, one workgroup each.
+struct PrefillPlan {
+  int tiles_n = 1;    // 128-column tiles along N
+  int tiles = 1;      // total tiles (= workgroups)
+};
+
+bool make_prefill_plan(int64_t M, int64_t K, int64_t N, PrefillPlan* plan);
+hipError_t launch_gemm_prefill(int bits, const PrefillPlan& p, const void* x,
+                               const void* packed, const void* scales, bool s_bf16,
+                               void* out, int64_t M, int64_t K, int64_t N,
+                               hipStream_t st);
+
 bool make_small_plan(int bits, int64_t M, int64_t K, int64_t N, int nbw, int wk,
                      int splits, SmallPlan* plan);
 size_t small_plan_workspace(const SmallPlan& p, int64_t M, int64_t N);

@@ -74,9 +74,41 @@ def test_small_shapes_every_plan(bits, M, K, N):
 @pytest.mark.parametrize("bits", [4, 8])
 @pytest.mark.parametrize("M", [17, 33, 64])
 def test_multi_row_blocks(bits, M):
+    """M > 16: the library's plan (prefill kernel) and the small-M kernel
+    over 16-row blocks (explicit plan) both match the oracle."""
     K, N = 512, 96
     x, c, s = _inputs(bits, M, K, N, 900 + M)
-    _assert_close(_run(bits, x, c, s, N), gemm.gemm_ref(x, c, s, SDT[bits]), "M=%d" % M)
+    ref = gemm.gemm_ref(x, c, s, SDT[bits])
+    _assert_close(_run(bits, x, c, s, N), ref, "M=%d prefill" % M)
+    _assert_close(_run(bits, x, c, s, N, plan=(1, 1, 1)), ref, "M=%d row blocks" % M)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("M,K,N", [(17, 128, 16), (129, 896, 592), (256, 1280, 2048),
+                                   (300, 384, 272), (1000, 256, 4096)])
+def test_prefill_shapes(bits, M, K, N):
+    """Prefill kernel: ragged 128 x 128 tiles in M and N, one-group K."""
+    x, c, s = _inputs(bits, M, K, N, 7 * M + N)
+    ref = gemm.gemm_ref(x, c, s, SDT[bits])
+    got = _run(bits, x, c, s, N)
+    _assert_close(got, ref, "prefill M=%d K=%d N=%d" % (M, K, N))
+    assert np.array_equal(got, _run(bits, x, c, s, N))      # deterministic
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_prefill_other_scale_dtype(bits):
+    """fp16 and bf16 scales are both accepted (configs use fp16 for INT4,
+    bf16 for INT8; the other pairing goes through the same kernels)."""
+    M, K, N = 200, 640, 320
+    other = "bf16" if bits == 4 else "f16"
+    x = workloads.activations(M, K, 5)
+    c = workloads.codes(K, N, bits, 6)
+    sb = workloads.scales(K // 128, N, other, 7)
+    pg = q.prepack(dev_i8(c), bits)
+    for m in (M, 1, 16):
+        out = q.qgemm(dev_bf16(x[:m]), pg, dev_scales(sb, other), bits, N)
+        got = numerics.bf16_to_f64(host_u16(out))
+        _assert_close(got, gemm.gemm_ref(x[:m], c, sb, other), "M=%d" % m)
 
 
 @pytest.mark.parametrize("bits", [4, 8])
