@@ -90,8 +90,13 @@ qg_status gemm(int bits, const void* x, const void* packed, const void* scales, 
   if (M > kSmallMaxM && !explicit_plan) {
     qg::PrefillPlan pp;
     if (!qg::make_prefill_plan(M, K, N, &pp)) return QG_ERR_SHAPE;
+    const size_t need = qg::prefill_workspace(bits, pp, K);
+    if (need > 0) {
+      if (ws == nullptr || ws_bytes < need) return QG_ERR_WORKSPACE;
+      if (!aligned16(ws)) return QG_ERR_ALIGN;
+    }
     return from_hip(qg::launch_gemm_prefill(bits, pp, x, packed, scales, s_dt == QG_BF16, out,
-                                            M, K, N, as_stream(stream)));
+                                            M, K, N, ws, as_stream(stream)));
   }
   qg::SmallPlan plan;
   if (!qg::make_small_plan(bits, M, K, N, nbw, wk, splits, &plan)) return QG_ERR_PLAN;
@@ -106,7 +111,11 @@ qg_status gemm(int bits, const void* x, const void* packed, const void* scales, 
 
 size_t workspace_bytes(int bits, int64_t M, int64_t K, int64_t N, int nbw, int wk, int splits) {
   if ((bits != 4 && bits != 8) || check_mkn(M, K, N) != QG_OK || M == 0) return 0;
-  if (M > kSmallMaxM && nbw == 0 && wk == 0 && splits == 0) return 0;   // prefill kernel
+  if (M > kSmallMaxM && nbw == 0 && wk == 0 && splits == 0) {   // prefill kernel
+    qg::PrefillPlan pp;
+    if (!qg::make_prefill_plan(M, K, N, &pp)) return 0;
+    return qg::prefill_workspace(bits, pp, K);
+  }
   qg::SmallPlan plan;
   if (!qg::make_small_plan(bits, M, K, N, nbw, wk, splits, &plan)) return 0;
   return qg::small_plan_workspace(plan, M, N);

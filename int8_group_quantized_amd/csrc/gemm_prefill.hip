@@ -2,27 +2,30 @@
 // of the speed paragraph of arXiv 2607.04244):
 //   out[m, n] = bf16( sum_g s[g, n] * sum_{k in g} x[m, k] * q[k, n] )
 //
-// At M = 8192 the product is a dense contraction (~2,000 flop per HBM byte),
-// so the kernel is bound by the bf16 matrix cores, not by memory:
-//   * a workgroup computes a 128 x 128 output tile with four wavefronts, each
-//     a 64 x 64 sub-tile as a 4 x 4 grid of 16x16 blocks;
-//   * the K loop steps one scale group (128) at a time. x for the group
-//     (128 rows x 128 K, 32 KiB of bf16) is staged in LDS with direct
-//     global->LDS loads, double-buffered, in the lane order of the
-//     16x16x32 A operand, so each wavefront reads its fragments with
-//     conflict-free 16-byte LDS reads; one barrier per group;
-//   * the packed weight tiles are already in B-operand order, so each
-//     wavefront loads its four 1 KiB (INT8: 2 KiB) column-block tiles of the
-//     next group straight into registers while the current group computes;
-//   * per group, each 16x16 block runs a four-instruction 16x16x32 chain
-//     into a scratch accumulator that is then scaled by the group's fp32
-//     scale and added to the running fp32 total (exact products, fp32 sums,
-//     as in the decode kernel). INT4 codes expand to 128 + u; the bias
-//     136 * sum x is one more chain per 16-row block, evaluated with the
-//     same instruction and operand order, so zero-code columns cancel to 0.
+// At M = 8192 the product is a dense contraction (~2,000 flop per HBM byte):
+// the bound is the bf16 matrix core, and what keeps the kernel from it is
+// (a) the per-CU load path (about 55 bytes per clock), (b) the vector ALU
+// work of unpacking codes and applying the per-group scale, and (c) waiting.
+//   * A workgroup of WN wavefronts computes a 64 x (64 WN) output tile; each
+//     wavefront a 64 x 64 sub-tile as a 4 x 4 grid of 16x16 blocks. Two or
+//     more workgroups share a CU, so while one waits at its barrier the
+//     other keeps the matrix core busy.
+//   * The K loop steps one scale group (128) at a time through a ring of
+//     LDS stages. A stage holds the group's x (64 rows, in the lane order of
+//     the 16x16x32 A operand), the 4 WN packed weight tiles (already in
+//     B-operand lane order), the group's scales and the 64 negated INT4
+//     offsets. Every byte arrives by a direct global->LDS load, and every
+//     wavefront issues the same number of them per stage, so "this stage
+//     has landed" is one vmcnt wait with a constant count and one barrier.
+//   * INT4 codes expand to bf16 128 + u with one and-or per pair; the
+//     offset 136 * sum_k x is computed once per (row, group) by a small
+//     pre-pass with the same matrix instruction and stored negated, and it
+//     seeds each block's 16x16x32 chain. The group total then leaves the
+//     matrix core as sum x * q, and one fma per element applies the fp32
+//     scale into the fp32 running sum (exact products, fp32 sums).
 // Tiles are mapped so that each XCD (workgroups are dealt to the eight XCDs
 // round-robin) walks a contiguous run of tiles with the column tile fastest:
-// the 128-row x slice it is working on stays in that XCD's L2 while the
+// the 64-row x slice it is working on stays in that XCD's L2 while the
 // packed weight streams past.
 #include "qg_device.h"
 #include "qg_internal.h"
@@ -30,11 +33,29 @@
 namespace qg {
 namespace {
 
-constexpr int kBM = 128;             // rows per workgroup tile
-constexpr int kBNB = 8;              // 16-column blocks per workgroup tile (128 columns)
-constexpr int kThreads = 256;        // four wavefronts, 2 x 2 over the tile
-constexpr int kRowBlocks = kBM / 16;
+constexpr int kBM = 64;                      // rows per workgroup tile
 constexpr int kXcds = 8;
+constexpr int kXBytes = kBM * kGroup * 2;    // one group of x for the tile: 16 KiB
+
+// One ring stage: x [16 blocks of 1 KiB], the 4 WN weight tiles, and per
+// wavefront 256 bytes of side data (64 scales, then 64 / WN negated offsets).
+template <int BITS, int WN, int NST>
+struct Stage {
+  static constexpr int kTile = (BITS == 4) ? 1024 : 2048;   // packed bytes per 16 x 128 tile
+  static constexpr int kB = kXBytes;                        // offset of the weight tiles
+  static constexpr int kSide = kB + 4 * WN * kTile;         // offset of the side data
+  static constexpr int kBytes = kSide + 256 * WN;
+  static constexpr int kXLoads = 16 / WN;
+  static constexpr int kBLoads = 4 * kTile / 1024;
+  static constexpr int kLoads = kXLoads + kBLoads + 1;      // direct loads per wavefront per stage
+  static constexpr int kRowsPerWave = kBM / WN;             // offsets loaded by one wavefront
+};
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+__device__ __forceinline__ void to_lds(const void* src, char* dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_ptr)dst, 16, 0, 0);
+}
 
 __device__ __forceinline__ bf16x8 int4_to_biased(uint32_t w, uint32_t magic) {
   const u32x4 r = {(w & 0x000F000Fu) | magic, ((w >> 4) & 0x000F000Fu) | magic,
@@ -42,27 +63,66 @@ __device__ __forceinline__ bf16x8 int4_to_biased(uint32_t w, uint32_t magic) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
+// The magic lives in a VGPR so that the and-or takes the mask as its one
+// scalar operand.
 __device__ __forceinline__ uint32_t opaque_bias_magic() {
   uint32_t m = 0x43004300u;
   asm volatile("" : "+v"(m));
   return m;
 }
 
-template <int BITS, bool SBF>
-__global__ __launch_bounds__(kThreads, 2) void gemm_prefill_kernel(
-    const uint16_t* __restrict__ x, const char* __restrict__ packed,
-    const uint16_t* __restrict__ scales, uint16_t* __restrict__ out, int M, int K, int N,
-    int tiles_n, int tiles) {
-  constexpr int TB = (BITS == 4) ? 1024 : 2048;   // bytes per packed tile
-  constexpr int TW = TB / 1024;                   // 16-byte words per lane per tile
-  // LDS: two buffers of [row block 8][K step 4][lane 64] 16-byte words.
-  __shared__ u32x4 xs[2][kRowBlocks * 4 * 64];
+// Fill one stage with group g. Wavefront w loads 16 / WN x blocks (row
+// block, K step), its four weight tiles (one 1 KiB piece per load), and
+// with one more load its side data: lanes 0-7 the scales of its 64 columns,
+// lanes 8.. the negated offsets of its 64 / WN rows (INT4 only).
+template <int BITS, int WN, int NST>
+__device__ __forceinline__ void load_stage(char* st, const uint16_t* __restrict__ x,
+                                           const char* __restrict__ packed,
+                                           const uint16_t* __restrict__ scales,
+                                           const float* __restrict__ nbias, int g, int wave,
+                                           int lane, int m0, int cb0, int M, int K, int N, int NB,
+                                           int G, int Mp) {
+  using S = Stage<BITS, WN, NST>;
+#pragma unroll
+  for (int i = 0; i < S::kXLoads; ++i) {
+    const int blk = wave * S::kXLoads + i;                     // = row block * 4 + K step
+    const int row = min(m0 + 16 * (blk >> 2) + (lane & 15), M - 1);   // rows past M: never stored
+    to_lds(x + (int64_t)row * K + g * kGroup + 32 * (blk & 3) + 8 * (lane >> 4),
+           st + blk * 1024);
+  }
+#pragma unroll
+  for (int i = 0; i < S::kBLoads; ++i) {
+    const int piece = wave * S::kBLoads + i;
+    const int cbl = piece / (S::kTile / 1024);
+    const int half = piece % (S::kTile / 1024);
+    const int cb = min(cb0 + cbl, NB - 1);                     // columns past N: never stored
+    to_lds(packed + ((int64_t)cb * G + g) * S::kTile + half * 1024 + lane * 16,
+           st + S::kB + piece * 1024);
+  }
+  constexpr int kBiasLanes = (BITS == 4) ? S::kRowsPerWave / 4 : 0;
+  if (lane < 8 + kBiasLanes) {
+    const void* src;
+    if (lane < 8) {
+      const int col = min(cb0 * 16 + 64 * wave + 8 * lane, N - 8);
+      src = scales + (int64_t)g * N + col;
+    } else {
+      src = nbias + (int64_t)g * Mp + m0 + S::kRowsPerWave * wave + 4 * (lane - 8);
+    }
+    to_lds(src, st + S::kSide + 256 * wave);
+  }
+}
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1;        // which 64-row half
-  const int wn = wave & 1;         // which 64-column half
+template <int BITS, bool SBF, int WN, int NST>
+__global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(2))) void gemm_prefill_kernel(
+    const uint16_t* __restrict__ x, const char* __restrict__ packed,
+    const uint16_t* __restrict__ scales, const float* __restrict__ nbias,
+    uint16_t* __restrict__ out, int M, int K, int N, int Mp, int tiles_n, int tiles) {
+  using S = Stage<BITS, WN, NST>;
+  extern __shared__ u32x4 smem[];
+  char* const lds = reinterpret_cast<char*>(smem);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // column quarter / half
   const int l16 = lane & 15;
   const int lq = lane >> 4;
   const int G = K >> 7;
@@ -76,38 +136,9 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_prefill_kernel(
   const int tm = t / tiles_n;
   const int tn = t - tm * tiles_n;
   const int m0 = tm * kBM;
-  const int cb_base = tn * kBNB + wn * 4;          // this wave's first column block
-
-  int cb[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) cb[c] = min(cb_base + c, NB - 1);   // clamped for loads
+  const int cb0 = tn * 4 * WN;
 
   const uint32_t magic = opaque_bias_magic();
-
-  // x staging: each wave fills 8 of the 32 (row block, K step) blocks of a
-  // group; lane l of a block holds row 16*rb + l%16, K 32*j + 8*(l/16) .. +7.
-  // Rows past M are clamped to M - 1 (their outputs are never stored).
-  auto stage_x = [&](int g, int buf) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int blk = wave * 8 + i;               // = rb * 4 + j
-      const int rb = blk >> 2;
-      const int j = blk & 3;
-      const int row = min(m0 + rb * 16 + l16, M - 1);
-      const uint16_t* src = x + (int64_t)row * K + (int64_t)g * 128 + 32 * j + 8 * lq;
-      __builtin_amdgcn_global_load_lds(
-          src, (__attribute__((address_space(3))) void*)(&xs[buf][blk * 64]), 16, 0, 0);
-    }
-  };
-  auto load_b = [&](int g, u32x4 (&bt)[4][TW], uint32_t (&sc)[4]) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const char* tp = packed + ((int64_t)cb[c] * G + g) * TB + lane * (TB / 64);
-#pragma unroll
-      for (int v = 0; v < TW; ++v) bt[c][v] = *reinterpret_cast<const u32x4*>(tp + 16 * v);
-      sc[c] = scales[(int64_t)g * N + cb[c] * 16 + l16];
-    }
-  };
 
   f32x4 acc[4][4];   // [column block][row block]
 #pragma unroll
@@ -115,117 +146,192 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_prefill_kernel(
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc[c][r] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  u32x4 bcur[4][TW], bnext[4][TW];
-  uint32_t scur[4], snext[4];
-  stage_x(0, 0);
-  load_b(0, bcur, scur);
+#pragma unroll
+  for (int s = 0; s < NST - 1; ++s)
+    if (s < G)
+      load_stage<BITS, WN, NST>(lds + s * S::kBytes, x, packed, scales, nbias, s, wave, lane, m0,
+                                cb0, M, K, N, NB, G, Mp);
 
+  int cur = 0;   // ring slot of group g
   for (int g = 0; g < G; ++g) {
-    const int buf = g & 1;
-    // This group's x and weights have landed (direct-to-LDS loads count in
-    // the vector-memory counter), and every wave is done with the other
-    // buffer, which the next group overwrites.
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (g + 1 < G) {
-      stage_x(g + 1, buf ^ 1);
-      load_b(g + 1, bnext, snext);
+    // Group g's stage has landed once only the loads of later stages (if
+    // any were issued) are outstanding; the barrier then publishes every
+    // wavefront's part and tells that all of them are done with the slot
+    // that the load below overwrites.
+    if (NST == 3 && g + 1 < G)
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(S::kLoads) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    const int ahead = g + NST - 1;
+    if (ahead < G) {
+      const int slot = (cur == 0) ? NST - 1 : cur - 1;
+      load_stage<BITS, WN, NST>(lds + slot * S::kBytes, x, packed, scales, nbias, ahead, wave,
+                                lane, m0, cb0, M, K, N, NB, G, Mp);
     }
+    const char* st = lds + cur * S::kBytes;
+    cur = (cur == NST - 1) ? 0 : cur + 1;
 
-    // A fragments of this wave's four row blocks, all four K steps.
     bf16x8 a[4][4];
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        a[r][j] = __builtin_bit_cast(bf16x8, xs[buf][((wm * 4 + r) * 4 + j) * 64 + lane]);
-
-    f32x4 bias[4];
+        a[r][j] = *reinterpret_cast<const bf16x8*>(st + (r * 4 + j) * 1024 + lane * 16);
+    f32x4 seed[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      bias[r] = f32x4{0.f, 0.f, 0.f, 0.f};
       if constexpr (BITS == 4) {
-        const bf16x8 b136 = bias136_bf16x8();
-#pragma unroll
-        for (int j = 0; j < 4; ++j) bias[r] = mfma16x16x32(a[r][j], b136, bias[r]);
+        const int rr = r * 16 + 4 * lq;   // first of this lane's four rows
+        seed[r] = *reinterpret_cast<const f32x4*>(
+            st + S::kSide + 256 * (rr / S::kRowsPerWave) + 128 + 4 * (rr % S::kRowsPerWave));
+      } else {
+        seed[r] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
     }
+    uint32_t sraw[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      sraw[c] = *reinterpret_cast<const uint16_t*>(st + S::kSide + 256 * wave + (c * 16 + l16) * 2);
 
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       bf16x8 bw[4];
+      if constexpr (BITS == 4) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(st + S::kB + (wave * 4 + c) * 1024 + lane * 16);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if constexpr (BITS == 4) {
-          bw[j] = int4_to_biased(bcur[c][0][j], magic);
-        } else {
-          const u32x4& w = bcur[c][j >> 1];
-          bw[j] = int8_words_to_bf16(w[(j & 1) * 2], w[(j & 1) * 2 + 1]);
-        }
+        for (int j = 0; j < 4; ++j) bw[j] = int4_to_biased(w[j], magic);
+      } else {
+        const char* tp = st + S::kB + (wave * 4 + c) * 2048 + lane * 32;
+        const u32x4 w0 = *reinterpret_cast<const u32x4*>(tp);
+        const u32x4 w1 = *reinterpret_cast<const u32x4*>(tp + 16);
+        bw[0] = int8_words_to_bf16(w0[0], w0[1]);
+        bw[1] = int8_words_to_bf16(w0[2], w0[3]);
+        bw[2] = int8_words_to_bf16(w1[0], w1[1]);
+        bw[3] = int8_words_to_bf16(w1[2], w1[3]);
       }
-      const float s = SBF ? bf16_bits_to_f32(scur[c]) : f16_bits_to_f32(scur[c]);
+      const float s = SBF ? bf16_bits_to_f32(sraw[c]) : f16_bits_to_f32(sraw[c]);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        f32x4 p = {0.f, 0.f, 0.f, 0.f};
+        f32x4 p = seed[r];
 #pragma unroll
         for (int j = 0; j < 4; ++j) p = mfma16x16x32(a[r][j], bw[j], p);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[c][r][e] = fmaf(s, p[e] - bias[r][e], acc[c][r][e]);
+        for (int e = 0; e < 4; ++e) acc[c][r][e] = fmaf(s, p[e], acc[c][r][e]);
       }
-    }
-
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      scur[c] = snext[c];
-#pragma unroll
-      for (int v = 0; v < TW; ++v) bcur[c][v] = bnext[c][v];
     }
   }
 
   // C layout of a 16x16 block: lane holds column l16, rows 4*lq + e.
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    if (cb_base + c >= NB) continue;
-    const int n = (cb_base + c) * 16 + l16;
+    const int cb = cb0 + wave * 4 + c;
+    if (cb >= NB) continue;
+    const int n = cb * 16 + l16;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int row = m0 + wm * 64 + r * 16 + 4 * lq + e;
+        const int row = m0 + r * 16 + 4 * lq + e;
         if (row < M) out[(int64_t)row * N + n] = f32_to_bf16_bits(acc[c][r][e]);
       }
     }
   }
 }
 
+// Negated INT4 offsets: nbias[g * Mp + m] = -(136 * sum_{k in g} x[m, k]),
+// formed by the same 16x16x32 chain (four K steps of 32, from zero) that the
+// main kernel continues from. One wavefront per (16-row block, group); rows
+// from M to Mp repeat row M - 1.
+__global__ __launch_bounds__(256) void prefill_bias_kernel(const uint16_t* __restrict__ x,
+                                                           float* __restrict__ nbias, int M, int K,
+                                                           int Mp, int units) {
+  const int lane = threadIdx.x & 63;
+  const int u = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (u >= units) return;
+  const int RB = Mp >> 4;
+  const int g = u / RB;
+  const int rb = u - g * RB;
+  const int row = min(rb * 16 + (lane & 15), M - 1);
+  const uint16_t* src = x + (int64_t)row * K + g * kGroup + 8 * (lane >> 4);
+  const bf16x8 b136 = bias136_bf16x8();
+  f32x4 p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    p = mfma16x16x32(*reinterpret_cast<const bf16x8*>(src + 32 * j), b136, p);
+  if ((lane & 15) == 0)
+    *reinterpret_cast<f32x4*>(nbias + (int64_t)g * Mp + rb * 16 + 4 * (lane >> 4)) = -p;
+}
+
+template <int BITS, bool SBF, int WN, int NST>
+void launch_main(const PrefillPlan& p, const uint16_t* x, const char* w, const uint16_t* s,
+                 const float* nb, uint16_t* out, int M, int K, int N, hipStream_t st) {
+  gemm_prefill_kernel<BITS, SBF, WN, NST>
+      <<<dim3((unsigned)p.tiles), 64 * WN, NST * Stage<BITS, WN, NST>::kBytes, st>>>(
+          x, w, s, nb, out, M, K, N, (int)p.mp, p.tiles_n, p.tiles);
+}
+
+template <int BITS, bool SBF>
+void launch_bits(const PrefillPlan& p, const uint16_t* x, const char* w, const uint16_t* s,
+                 const float* nb, uint16_t* out, int M, int K, int N, hipStream_t st) {
+  if (p.wn == 4) launch_main<BITS, SBF, 4, 2>(p, x, w, s, nb, out, M, K, N, st);
+  else           launch_main<BITS, SBF, 2, 2>(p, x, w, s, nb, out, M, K, N, st);
+}
+
+constexpr int kCUs = 256;   // MI355X compute units (plan heuristic only)
+
 }  // namespace
 
+// Tile width: 256 columns (four wavefronts, two workgroups per CU) unless
+// 128 columns (two wavefronts, three per CU) fills the last round of
+// workgroups better.
 bool make_prefill_plan(int64_t M, int64_t K, int64_t N, PrefillPlan* plan) {
-  (void)K;
   const int64_t tiles_m = (M + kBM - 1) / kBM;
-  const int64_t tiles_n = (N / kTileCols + kBNB - 1) / kBNB;
-  const int64_t tiles = tiles_m * tiles_n;
-  if (tiles > 0x7FFFFFFF) return false;
-  plan->tiles_n = (int)tiles_n;
-  plan->tiles = (int)tiles;
+  const int64_t NB = N / kTileCols;
+  double best = -1.0;
+  for (int wn : {4, 2}) {
+    const int64_t tiles = tiles_m * ((NB + 4 * wn - 1) / (4 * wn));
+    const int64_t slots = (int64_t)kCUs * (wn == 4 ? 2 : 3);
+    const int64_t rounds = (tiles + slots - 1) / slots;
+    // useful fraction of the occupied slot-rounds, with the narrower tile's
+    // extra x traffic priced at 15%
+    const double eff = (double)tiles / (double)(rounds * slots) * (wn == 4 ? 1.0 : 0.85);
+    if (tiles > 0x7FFFFFFF) return false;
+    if (eff > best + 1e-9) {
+      best = eff;
+      plan->wn = wn;
+      plan->tiles_n = (int)((NB + 4 * wn - 1) / (4 * wn));
+      plan->tiles = (int)tiles;
+    }
+  }
+  plan->mp = tiles_m * kBM;
+  if (plan->mp * (K / kGroup) > 0x7FFFFFFF) return false;
   return true;
+}
+
+size_t prefill_workspace(int bits, const PrefillPlan& p, int64_t K) {
+  if (bits != 4) return 0;
+  return (size_t)kCounterBytes + (size_t)p.mp * (size_t)(K / kGroup) * sizeof(float);
 }
 
 hipError_t launch_gemm_prefill(int bits, const PrefillPlan& p, const void* x, const void* packed,
                                const void* scales, bool s_bf16, void* out, int64_t M, int64_t K,
-                               int64_t N, hipStream_t st) {
-  const dim3 grid((unsigned)p.tiles);
+                               int64_t N, void* ws, hipStream_t st) {
   const auto* xp = static_cast<const uint16_t*>(x);
   const auto* wp = static_cast<const char*>(packed);
   const auto* sp = static_cast<const uint16_t*>(scales);
   auto* op = static_cast<uint16_t*>(out);
   const int m = (int)M, k = (int)K, n = (int)N;
   if (bits == 4) {
-    if (s_bf16) gemm_prefill_kernel<4, true><<<grid, kThreads, 0, st>>>(xp, wp, sp, op, m, k, n, p.tiles_n, p.tiles);
-    else        gemm_prefill_kernel<4, false><<<grid, kThreads, 0, st>>>(xp, wp, sp, op, m, k, n, p.tiles_n, p.tiles);
+    // The offsets sit after the arrival counters, which stay untouched.
+    float* nb = reinterpret_cast<float*>(static_cast<char*>(ws) + kCounterBytes);
+    const int units = (int)(p.mp / 16 * (K / kGroup));
+    prefill_bias_kernel<<<dim3((unsigned)((units + 3) / 4)), 256, 0, st>>>(xp, nb, m, k,
+                                                                           (int)p.mp, units);
+    if (s_bf16) launch_bits<4, true>(p, xp, wp, sp, nb, op, m, k, n, st);
+    else        launch_bits<4, false>(p, xp, wp, sp, nb, op, m, k, n, st);
   } else {
-    if (s_bf16) gemm_prefill_kernel<8, true><<<grid, kThreads, 0, st>>>(xp, wp, sp, op, m, k, n, p.tiles_n, p.tiles);
-    else        gemm_prefill_kernel<8, false><<<grid, kThreads, 0, st>>>(xp, wp, sp, op, m, k, n, p.tiles_n, p.tiles);
+    if (s_bf16) launch_bits<8, true>(p, xp, wp, sp, nullptr, op, m, k, n, st);
+    else        launch_bits<8, false>(p, xp, wp, sp, nullptr, op, m, k, n, st);
   }
   return hipGetLastError();
 }

@@ -29,14 +29,18 @@ struct SmallPlan {
 
 // Large-M (prefill) tiling: 128 x 128 output tiles, one workgroup each.
 struct PrefillPlan {
-  int tiles_n = 1;    // 128-column tiles along N
+  int wn = 4;         // wavefronts per workgroup = 64-column sub-tiles per tile
+  int tiles_n = 1;    // 64 * wn-column tiles along N
   int tiles = 1;      // total tiles (= workgroups)
+  int64_t mp = 64;    // M rounded up to the 64-row tile
 };
 
 bool make_prefill_plan(int64_t M, int64_t K, int64_t N, PrefillPlan* plan);
+// Workspace bytes of the prefill path (INT4: counters area + negated offsets).
+size_t prefill_workspace(int bits, const PrefillPlan& p, int64_t K);
 hipError_t launch_gemm_prefill(int bits, const PrefillPlan& p, const void* x,
                                const void* packed, const void* scales, bool s_bf16,
-                               void* out, int64_t M, int64_t K, int64_t N,
+                               void* out, int64_t M, int64_t K, int64_t N, void* ws,
                                hipStream_t st);
 
 bool make_small_plan(int bits, int64_t M, int64_t K, int64_t N, int nbw, int wk,

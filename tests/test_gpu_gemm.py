@@ -147,6 +147,29 @@ def test_exact_zeros(bits):
 
 
 @pytest.mark.parametrize("bits", [4, 8])
+def test_prefill_zero_codes_and_scales(bits):
+    """Prefill path: zero scales and zero activations give exact zeros; an
+    all-zero INT4 code column leaves only the fp32 rounding of the 136 * sum x
+    offset it cancels (at most a few ulp of 136 * sum |x| per group)."""
+    M, K, N = 200, 640, 320
+    x, c, s = _inputs(bits, M, K, N, 63)
+    c[:, :16] = 0
+    s = s.copy()
+    s[:, 16:32] = 0
+    got = _run(bits, x, c, s, N)
+    assert np.all(got[:, 16:32] == 0)
+    xs = numerics.bf16_to_f64(x)
+    sv = numerics.scale_bits_to_f64(s, SDT[bits])
+    gsum = np.abs(xs).reshape(M, K // 128, 128).sum(axis=2)          # [M, G]
+    bound = 8 * 2.0 ** -24 * 136 * gsum @ np.abs(sv[:, :16])          # [M, 16]
+    if bits == 8:
+        bound[:] = 0
+    assert np.all(np.abs(got[:, :16]) <= bound)
+    _assert_close(got, gemm.gemm_ref(x, c, s, SDT[bits]))
+    assert np.all(_run(bits, np.zeros_like(x), c, s, N) == 0)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
 def test_range_ends_and_large_activations(bits):
     M, K, N = 16, 1024, 128
     x, c, s = _inputs(bits, M, K, N, 71, xstd=3e3)
