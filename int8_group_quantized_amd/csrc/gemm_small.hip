@@ -12,14 +12,19 @@
 //   * a wavefront owns NBW 16-column blocks and a contiguous run of K groups,
 //     walked in batches of D groups held in two register buffers: while one
 //     batch is multiplied the next is being fetched. Each tile is one
-//     16-byte load per lane (a tile is contiguous, so the load is a fully
-//     coalesced 1 KiB transaction) addressed as a wave-uniform base plus a
-//     fixed lane offset; the loop body is straight-line code, so the wait
-//     counters keep a fixed number of loads in flight;
+//     16-byte buffer load per lane (a tile is contiguous, so the load is a
+//     fully coalesced 1 KiB transaction) through a per-wavefront buffer
+//     resource that covers exactly the wavefront's remaining groups, so a
+//     fetch past the last group returns zeros without touching memory. The
+//     loop body is therefore straight-line code with no redundant traffic,
+//     and the wait counters keep a fixed number of loads in flight;
 //   * the workgroup stages its slice of x in LDS with direct global->LDS
 //     loads, in the lane order of the matrix-core A operand, with rows >= M
 //     stored as zeros (MR = 16) or read from a zero block (MR = 1), so each
-//     group is four unconditional 16-byte LDS reads at immediate offsets;
+//     group is four unconditional 16-byte LDS reads at immediate offsets.
+//     The scales of the workgroup's columns are staged beside x. These
+//     staging loads go out before the weight tiles, so waiting for them
+//     does not wait for the tiles;
 //   * codes expand in registers to exact bf16 integers (seven ALU ops per
 //     eight INT4 codes, twelve per eight INT8 codes); four 16x16x32 bf16
 //     matrix-core ops give a group's fp32 partial sums for 16 rows x 16
@@ -46,7 +51,8 @@ namespace qg {
 namespace {
 
 constexpr int kMaxCounters = kCounterBytes / sizeof(uint32_t);
-constexpr int64_t kLdsBudget = 80 * 1024;   // dynamic LDS per workgroup (two per CU)
+constexpr int64_t kLdsAuto = 80 * 1024;     // LDS per workgroup the library's own plans use
+constexpr int64_t kLdsMax = 160 * 1024;     // LDS a workgroup may have (explicit plans)
 
 // Device-coherent (agent scope) accesses for the split-K partials.
 __device__ __forceinline__ void store_coherent(float* p, float v) {
@@ -76,6 +82,19 @@ __device__ __forceinline__ uint32_t opaque_magic() {
   return m;
 }
 
+// s_waitcnt immediate (gfx9 encoding) for "at most n vector-memory loads
+// outstanding, all LDS operations done". Issued through the builtin so that
+// the compiler's own wait-count tracking sees it.
+constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
+
+// Raw buffer resource (no stride, no swizzle): loads at byte offsets at or
+// past num_records return zeros and make no memory access.
+constexpr int kRsrcWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRsrcWord3);
+}
+
 template <int BITS>
 struct Tile {
   static constexpr int bytes = (BITS == 4) ? 1024 : 2048;
@@ -93,7 +112,7 @@ struct Batch {
 
 template <int BITS, bool SBF, int MR, int NBW, int WN, int WK>
 __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_small_kernel(
-    const uint16_t* __restrict__ x, const char* __restrict__ packed,
+    const uint16_t* __restrict__ x, const char* packed,
     const uint16_t* __restrict__ scales, uint16_t* __restrict__ out,
     uint32_t* __restrict__ counters, float* __restrict__ partials, int M, int K, int N,
     int splits, int gps, int sg) {
@@ -121,12 +140,16 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_small_kernel(
   const int wg_gn = min(G, wg_g0 + gps) - wg_g0;
   const int l16 = lane & 15;                 // A row / C column of this lane
   const int lq = lane >> 4;                  // K slice (A, B) / row quad (C)
-  u32x4* xs = smem;                          // [sg][XG] x fragments, then a zero block
+  constexpr int SC = WN * NBW * 16;          // scale columns staged per group
+  u32x4* xs = smem;                          // [sg][XG] x fragments, then a zero block (MR == 1)
+  const uint16_t* ss =                       // [sg][SC] scales of the workgroup's columns
+      reinterpret_cast<const uint16_t*>(smem + sg * XG + (MR == 1 ? 16 : 0));
+  const int cbw = blockIdx.x * WN * NBW;     // first column block of the workgroup
   const uint32_t magic = opaque_magic();
 
   int cb[NBW];
 #pragma unroll
-  for (int c = 0; c < NBW; ++c) cb[c] = min(cb0 + c, NB - 1);   // clamped: loads stay in range
+  for (int c = 0; c < NBW; ++c) cb[c] = min(cb0 + c, NB - 1);   // clamped: stays in range
   const int lane_off = lane * (TB / 64);
   // x fragment address of this lane for stage group 0, and its per-group step
   // (in 16-byte words); with MR == 1 only lanes of row 0 read data, the rest
@@ -138,33 +161,34 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_small_kernel(
 #pragma unroll
   for (int c = 0; c < NBW; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int s0 = 0; s0 < wg_gn; s0 += sg) {
-    const int sn = min(sg, wg_gn - s0);
+  {
+    // One stage: the workgroup's whole K range is staged at once.
+    constexpr int s0 = 0;
+    const int sn = wg_gn;
     const int per = (sn + WK - 1) / WK;
     const int w_lo = min(sn, wk * per);
     const int w_n = min(sn, w_lo + per) - w_lo;   // may be 0 for trailing waves
     const int g_first = wg_g0 + s0 + w_lo;
-    const int g_last = wg_g0 + s0 + max(w_lo + w_n - 1, 0);
     const int nbatch = (w_n + D - 1) / D;
 
     u32x4 ta[D][NBW][TW], tb[D][NBW][TW];
-    uint32_t sa[D][NBW], sb[D][NBW];
-    // Batch b: groups g_first + b*D + d, clamped to g_last (extra ones are
-    // recomputed and weighted by zero).
-    auto load_batch = [&](int b, u32x4 (&t)[D][NBW][TW], uint32_t (&s)[D][NBW]) {
+    // Batch b: groups g_first + b*D + d of each column block, through a
+    // resource that ends at the wavefront's last group (later ones read 0).
+    auto load_batch = [&](int b, u32x4 (&t)[D][NBW][TW]) {
+      const int i0 = min(b * D, w_n);
 #pragma unroll
-      for (int d = 0; d < D; ++d) {
-        const int g = min(g_first + b * D + d, g_last);
+      for (int c = 0; c < NBW; ++c) {
+        const __amdgpu_buffer_rsrc_t r =
+            make_rsrc(packed + ((int64_t)cb[c] * G + g_first + i0) * TB, (w_n - i0) * TB);
 #pragma unroll
-        for (int c = 0; c < NBW; ++c) {
-          const char* tp = packed + ((int64_t)cb[c] * G + g) * TB + lane_off;
+        for (int d = 0; d < D; ++d)
 #pragma unroll
-          for (int v = 0; v < TW; ++v) t[d][c][v] = *reinterpret_cast<const u32x4*>(tp + 16 * v);
-          s[d][c] = scales[(int64_t)g * N + cb[c] * 16 + l16];
-        }
+          for (int v = 0; v < TW; ++v)
+            t[d][c][v] = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, lane_off + d * TB + 16 * v, 0, 0));
       }
     };
-    auto compute_batch = [&](int b, const u32x4 (&t)[D][NBW][TW], const uint32_t (&s)[D][NBW]) {
+    auto compute_batch = [&](int b, const u32x4 (&t)[D][NBW][TW]) {
 #pragma unroll
       for (int d = 0; d < D; ++d) {
         const int i = b * D + d;                      // wave-relative group
@@ -180,6 +204,7 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_small_kernel(
 #pragma unroll
           for (int j = 0; j < 4; ++j) bias = mfma16x16x32(a[j], b136, bias);
         }
+        const uint16_t* sp = ss + gl * SC + wn * NBW * 16 + l16;
 #pragma unroll
         for (int c = 0; c < NBW; ++c) {
           f32x4 p = {0.f, 0.f, 0.f, 0.f};
@@ -193,7 +218,8 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_small_kernel(
             p = mfma16x16x32(a[2], int8_words_to_bf16(t[d][c][1][0], t[d][c][1][1]), p);
             p = mfma16x16x32(a[3], int8_words_to_bf16(t[d][c][1][2], t[d][c][1][3]), p);
           }
-          const float sv = SBF ? bf16_bits_to_f32(s[d][c]) : f16_bits_to_f32(s[d][c]);
+          const uint32_t sbits = sp[c * 16];
+          const float sv = SBF ? bf16_bits_to_f32(sbits) : f16_bits_to_f32(sbits);
           const float scale = live ? sv : 0.0f;
           if constexpr (MR == 1) {
             // One live row: only element 0 of the lanes holding rows 0..3 is
@@ -207,16 +233,22 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_small_kernel(
       }
     };
 
-    // Both register batches in flight while x is staged.
-    load_batch(0, ta, sa);
-    load_batch(1, tb, sb);
-    if (s0 > 0) __syncthreads();             // every wave is done with the last stage
     {
       // Stage x with direct global->LDS loads: one wavefront instruction fills
       // one contiguous 1 KiB block of the layout (lane l -> 16 bytes at l*16).
       // Slots of rows >= M are written with zeros by the lanes that skip the
       // load, so no slot is written twice.
       const int total = sn * XG;                      // 16-byte words to fill
+      // Zero slots first (rows >= M, and the zero block that rows >= 1 read
+      // when MR == 1), then the direct loads, so no LDS write follows a
+      // direct load that might still be landing.
+      if constexpr (MR == 16) {
+        if (mrows < 16)
+          for (int e = tid; e < total; e += NT)
+            if ((e & 15) >= mrows) xs[e] = u32x4{0u, 0u, 0u, 0u};
+      } else {
+        if (tid < 16) xs[sg * XG + tid] = u32x4{0u, 0u, 0u, 0u};
+      }
       for (int w0 = wave * 64; w0 < total; w0 += NW * 64) {
         const int e = w0 + lane;
         int g, j, q, r;
@@ -225,38 +257,58 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_small_kernel(
         } else {
           g = e >> 8; j = (e >> 6) & 3; q = (e >> 4) & 3; r = e & 15;
         }
-        if (e < total) {
-          if (r < mrows) {
-            const uint16_t* src = x + (int64_t)(row0 + r) * K + (int64_t)(wg_g0 + s0 + g) * 128 +
-                                  32 * j + 8 * q;
-            __builtin_amdgcn_global_load_lds(
-                src, (__attribute__((address_space(3))) void*)(xs + w0), 16, 0, 0);
-          } else {
-            xs[e] = u32x4{0u, 0u, 0u, 0u};
-          }
+        if (e < total && r < mrows) {
+          const uint16_t* src = x + (int64_t)(row0 + r) * K + (int64_t)(wg_g0 + s0 + g) * 128 +
+                                32 * j + 8 * q;
+          __builtin_amdgcn_global_load_lds(
+              src, (__attribute__((address_space(3))) void*)(xs + w0), 16, 0, 0);
         }
       }
-      if constexpr (MR == 1) {
-        if (tid < 16) xs[sg * XG + tid] = u32x4{0u, 0u, 0u, 0u};   // zero block for rows >= 1
+      // Scales: SC / 8 sixteen-byte pieces per group; columns past N read the
+      // last valid piece (their outputs are never stored).
+      constexpr int PPG = SC / 8;
+      const int ptotal = sn * PPG;
+      u32x4* sdst = smem + sg * XG + (MR == 1 ? 16 : 0);
+      for (int w0 = wave * 64; w0 < ptotal; w0 += NW * 64) {
+        const int e = w0 + lane;
+        if (e < ptotal) {
+          const int g = e / PPG;
+          const int col = min(cbw * 16 + (e - g * PPG) * 8, N - 8);
+          __builtin_amdgcn_global_load_lds(scales + (int64_t)(wg_g0 + s0 + g) * N + col,
+                                           (__attribute__((address_space(3))) void*)(sdst + w0),
+                                           16, 0, 0);
+        }
       }
     }
-    // The direct-to-LDS loads (and, with them, both tile batches) must land
-    // before any wavefront reads the staged x.
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+    // Both tile batches go out after the staging loads (the empty asm keeps
+    // the compiler from hoisting them); waiting until no more than their
+    // count is outstanding then waits for the staging only, and the zero
+    // slots written through LDS are complete before the barrier.
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    load_batch(0, ta);
+    load_batch(1, tb);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * D * NBW * TW));
+    asm volatile("s_barrier" ::: "memory");
 
     if (w_n > 0) {
       // Batches in pairs: multiply one while the other is in flight. The loop
-      // body is straight-line code (fetches past the wave's last group are
-      // clamped, redundant and discarded); an odd last batch runs on its own.
+      // body is straight-line code (fetches past the wave's last group return
+      // zeros and touch no memory); an odd last batch runs on its own.
       int b = 0;
       for (; b + 1 < nbatch; b += 2) {
-        compute_batch(b, ta, sa);
-        load_batch(b + 2, ta, sa);
-        compute_batch(b + 1, tb, sb);
-        load_batch(b + 3, tb, sb);
+        compute_batch(b, ta);
+        __builtin_amdgcn_sched_barrier(0);
+        load_batch(b + 2, ta);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_batch(b + 1, tb);
+        __builtin_amdgcn_sched_barrier(0);
+        load_batch(b + 3, tb);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      if (b < nbatch) compute_batch(b, ta, sa);
+      if (b < nbatch) compute_batch(b, ta);
     }
   }
 
@@ -388,18 +440,17 @@ bool shape_supported(int nbw, int wn, int wk) {
   return false;
 }
 
-// LDS bytes per stage group: x fragments, rows padded to 16 unless M == 1.
-int64_t lds_per_group(int bits, int wn, int mr) {
-  (void)bits;
-  (void)wn;
-  return mr == 1 ? 256 : 4096;
+// LDS bytes per stage group: x fragments (rows padded to 16 unless M == 1)
+// and the scales of the workgroup's columns.
+int64_t lds_per_group(int wn, int nbw, int mr) {
+  return (mr == 1 ? 256 : 4096) + (int64_t)wn * nbw * 16 * 2;
 }
 
 }  // namespace
 
 size_t small_plan_lds_bytes(const SmallPlan& p, int64_t M) {
   (void)M;
-  const size_t stage = (size_t)p.sg * (size_t)lds_per_group(p.bits, p.wn, p.mr) + 256;
+  const size_t stage = (size_t)p.sg * (size_t)lds_per_group(p.wn, p.nbw, p.mr) + 256;
   const size_t red = (size_t)(p.wk - 1) * p.wn * p.nbw * 64 * 16;
   return stage > red ? stage : red;
 }
@@ -424,21 +475,21 @@ bool make_small_plan(int bits, int64_t M, int64_t K, int64_t N, int nbw, int wk,
   p.wk = wk;
   p.wn = wn;
   p.wgs_n = (int)((NB + (int64_t)wn * nbw - 1) / ((int64_t)wn * nbw));
-  const int64_t max_sg = (kLdsBudget - 256) / lds_per_group(bits, wn, p.mr);
+  // The workgroup stages x and the scales for its whole K range at once.
+  // The library's plans split K across workgroups so that this fits two
+  // workgroups per CU; explicit plans may use up to a CU's LDS.
+  const int64_t per_group = lds_per_group(wn, nbw, p.mr);
   if (splits == 0) {
-    // Split K across workgroups when one workgroup's x slice would not fit
-    // in LDS (M <= 16 only: beyond that, stages avoid a large workspace).
-    splits = (M <= 16) ? (int)((G + max_sg - 1) / max_sg) : 1;
+    const int64_t fit = (kLdsAuto - 256) / per_group;
+    splits = (int)((G + fit - 1) / fit);
   }
   if (splits < 1 || splits > G) return false;
   p.gps = (int)((G + splits - 1) / splits);
   p.splits = (int)((G + p.gps - 1) / p.gps);   // no empty split
-  // Stage size: as many groups as fit the LDS budget, balanced across stages.
-  const int64_t stages = (p.gps + max_sg - 1) / max_sg;
-  p.sg = (int)((p.gps + stages - 1) / stages);
+  p.sg = p.gps;
   if (p.splits > 65535 || p.row_blocks > 65535) return false;
   if (p.splits > 1 && (int64_t)p.wgs_n * p.row_blocks > kMaxCounters) return false;
-  if ((int64_t)small_plan_lds_bytes(p, M) > kLdsBudget) return false;
+  if ((int64_t)small_plan_lds_bytes(p, M) > kLdsMax) return false;
   *plan = p;
   return true;
 }
