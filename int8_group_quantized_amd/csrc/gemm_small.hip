@@ -44,6 +44,8 @@
 // partials with device-coherent stores, count arrivals with one atomic, and
 // the last to arrive sums the partials in split order (no whole-cache flush
 // or invalidate is needed: the partials never sit in a non-coherent cache).
+#include <algorithm>
+
 #include "qg_device.h"
 #include "qg_internal.h"
 
@@ -463,6 +465,24 @@ bool make_small_plan(int bits, int64_t M, int64_t K, int64_t N, int nbw, int wk,
   p.bits = bits;
   p.mr = (M == 1) ? 1 : 16;
   p.row_blocks = (int)((M + 15) / 16);
+  const bool own = (nbw == 0 && wk == 0 && splits == 0);
+  if (own) {
+    // The library's own plan, from sweeps of the decode and verification
+    // shapes on MI355X: one column block per wavefront and four wavefronts
+    // splitting K for one row; for 2-16 rows, wide N shares each staged x
+    // group between eight column blocks (two per wavefront), long K splits
+    // across three workgroups with two K-wavefronts each, and the rest use
+    // four K-wavefronts per column block.
+    if (M == 1) {
+      nbw = 1; wk = 4;
+    } else if (NB >= 1024) {
+      nbw = 2; wk = 1; splits = 1;
+    } else if (G >= 40) {
+      nbw = 1; wk = 2; splits = (int)((G + 25) / 26);
+    } else {
+      nbw = 1; wk = 4;
+    }
+  }
   if (nbw == 0) nbw = 1;
   if (wk == 0) {
     // Enough column-block waves to fill the chip without splitting K, else
@@ -480,8 +500,13 @@ bool make_small_plan(int bits, int64_t M, int64_t K, int64_t N, int nbw, int wk,
   // workgroups per CU; explicit plans may use up to a CU's LDS.
   const int64_t per_group = lds_per_group(wn, nbw, p.mr);
   if (splits == 0) {
-    const int64_t fit = (kLdsAuto - 256) / per_group;
+    // The own plan may use up to a CU's LDS; other plans keep two
+    // workgroups per CU.
+    const int64_t fit = ((own ? kLdsMax - 512 : kLdsAuto - 256)) / per_group;
     splits = (int)((G + fit - 1) / fit);
+  } else if (own) {
+    const int64_t fit = (kLdsMax - 512) / per_group;
+    splits = (int)std::max<int64_t>(splits, (G + fit - 1) / fit);
   }
   if (splits < 1 || splits > G) return false;
   p.gps = (int)((G + splits - 1) / splits);
