@@ -22,9 +22,10 @@
 //     loads, in the lane order of the matrix-core A operand, with rows >= M
 //     stored as zeros (MR = 16) or read from a zero block (MR = 1), so each
 //     group is four unconditional 16-byte LDS reads at immediate offsets.
-//     The scales of the workgroup's columns are staged beside x. These
-//     staging loads go out before the weight tiles, so waiting for them
-//     does not wait for the tiles;
+//     The staging loads go out before the weight tiles, so waiting for them
+//     does not wait for the tiles. Scales travel with the tiles (one 2-byte
+//     buffer load per tile and lane), so the cold scale rows are never
+//     waited for before the first multiply;
 //   * codes expand in registers to exact bf16 integers (seven ALU ops per
 //     eight INT4 codes, twelve per eight INT8 codes); four 16x16x32 bf16
 //     matrix-core ops give a group's fp32 partial sums for 16 rows x 16
@@ -114,8 +115,8 @@ struct Batch {
 
 template <int BITS, bool SBF, int MR, int NBW, int WN, int WK>
 __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_small_kernel(
-    const uint16_t* __restrict__ x, const char* packed,
-    const uint16_t* __restrict__ scales, uint16_t* __restrict__ out,
+    const uint16_t* __restrict__ x, const char* packed, const uint16_t* scales,
+    uint16_t* __restrict__ out,
     uint32_t* __restrict__ counters, float* __restrict__ partials, int M, int K, int N,
     int splits, int gps, int sg) {
   constexpr int NT = 64 * WN * WK;
@@ -142,17 +143,14 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_small_kernel(
   const int wg_gn = min(G, wg_g0 + gps) - wg_g0;
   const int l16 = lane & 15;                 // A row / C column of this lane
   const int lq = lane >> 4;                  // K slice (A, B) / row quad (C)
-  constexpr int SC = WN * NBW * 16;          // scale columns staged per group
   u32x4* xs = smem;                          // [sg][XG] x fragments, then a zero block (MR == 1)
-  const uint16_t* ss =                       // [sg][SC] scales of the workgroup's columns
-      reinterpret_cast<const uint16_t*>(smem + sg * XG + (MR == 1 ? 16 : 0));
-  const int cbw = blockIdx.x * WN * NBW;     // first column block of the workgroup
   const uint32_t magic = opaque_magic();
 
   int cb[NBW];
 #pragma unroll
   for (int c = 0; c < NBW; ++c) cb[c] = min(cb0 + c, NB - 1);   // clamped: stays in range
   const int lane_off = lane * (TB / 64);
+  const int s_off = l16 * 2;                 // this lane's scale within a tile's 16
   // x fragment address of this lane for stage group 0, and its per-group step
   // (in 16-byte words); with MR == 1 only lanes of row 0 read data, the rest
   // read the zero block.
@@ -174,23 +172,31 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_small_kernel(
     const int nbatch = (w_n + D - 1) / D;
 
     u32x4 ta[D][NBW][TW], tb[D][NBW][TW];
-    // Batch b: groups g_first + b*D + d of each column block, through a
-    // resource that ends at the wavefront's last group (later ones read 0).
-    auto load_batch = [&](int b, u32x4 (&t)[D][NBW][TW]) {
+    uint32_t sa[D][NBW], sb[D][NBW];
+    // Batch b: groups g_first + b*D + d of each column block, through
+    // resources that end at the wavefront's last group (later ones read 0):
+    // the tiles, and the 16 scales of each tile (one per lane column).
+    auto load_batch = [&](int b, u32x4 (&t)[D][NBW][TW], uint32_t (&sc)[D][NBW]) {
       const int i0 = min(b * D, w_n);
+      const int left = w_n - i0;                      // groups still in range
 #pragma unroll
       for (int c = 0; c < NBW; ++c) {
         const __amdgpu_buffer_rsrc_t r =
-            make_rsrc(packed + ((int64_t)cb[c] * G + g_first + i0) * TB, (w_n - i0) * TB);
+            make_rsrc(packed + ((int64_t)cb[c] * G + g_first + i0) * TB, left * TB);
+        const __amdgpu_buffer_rsrc_t rs =
+            make_rsrc(scales + (int64_t)(g_first + i0) * N + cb[c] * 16,
+                      left > 0 ? (left - 1) * N * 2 + 32 : 0);
 #pragma unroll
-        for (int d = 0; d < D; ++d)
+        for (int d = 0; d < D; ++d) {
 #pragma unroll
           for (int v = 0; v < TW; ++v)
             t[d][c][v] = __builtin_bit_cast(
                 u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, lane_off + d * TB + 16 * v, 0, 0));
+          sc[d][c] = __builtin_amdgcn_raw_buffer_load_b16(rs, s_off + d * N * 2, 0, 0);
+        }
       }
     };
-    auto compute_batch = [&](int b, const u32x4 (&t)[D][NBW][TW]) {
+    auto compute_batch = [&](int b, const u32x4 (&t)[D][NBW][TW], const uint32_t (&sc)[D][NBW]) {
 #pragma unroll
       for (int d = 0; d < D; ++d) {
         const int i = b * D + d;                      // wave-relative group
@@ -206,7 +212,6 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_small_kernel(
 #pragma unroll
           for (int j = 0; j < 4; ++j) bias = mfma16x16x32(a[j], b136, bias);
         }
-        const uint16_t* sp = ss + gl * SC + wn * NBW * 16 + l16;
 #pragma unroll
         for (int c = 0; c < NBW; ++c) {
           f32x4 p = {0.f, 0.f, 0.f, 0.f};
@@ -220,7 +225,7 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_small_kernel(
             p = mfma16x16x32(a[2], int8_words_to_bf16(t[d][c][1][0], t[d][c][1][1]), p);
             p = mfma16x16x32(a[3], int8_words_to_bf16(t[d][c][1][2], t[d][c][1][3]), p);
           }
-          const uint32_t sbits = sp[c * 16];
+          const uint32_t sbits = sc[d][c];
           const float sv = SBF ? bf16_bits_to_f32(sbits) : f16_bits_to_f32(sbits);
           const float scale = live ? sv : 0.0f;
           if constexpr (MR == 1) {
@@ -266,21 +271,6 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_small_kernel(
               src, (__attribute__((address_space(3))) void*)(xs + w0), 16, 0, 0);
         }
       }
-      // Scales: SC / 8 sixteen-byte pieces per group; columns past N read the
-      // last valid piece (their outputs are never stored).
-      constexpr int PPG = SC / 8;
-      const int ptotal = sn * PPG;
-      u32x4* sdst = smem + sg * XG + (MR == 1 ? 16 : 0);
-      for (int w0 = wave * 64; w0 < ptotal; w0 += NW * 64) {
-        const int e = w0 + lane;
-        if (e < ptotal) {
-          const int g = e / PPG;
-          const int col = min(cbw * 16 + (e - g * PPG) * 8, N - 8);
-          __builtin_amdgcn_global_load_lds(scales + (int64_t)(wg_g0 + s0 + g) * N + col,
-                                           (__attribute__((address_space(3))) void*)(sdst + w0),
-                                           16, 0, 0);
-        }
-      }
     }
     // Both tile batches go out after the staging loads (the empty asm keeps
     // the compiler from hoisting them); waiting until no more than their
@@ -288,11 +278,11 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_small_kernel(
     // slots written through LDS are complete before the barrier.
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
-    load_batch(0, ta);
-    load_batch(1, tb);
+    load_batch(0, ta, sa);
+    load_batch(1, tb, sb);
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * D * NBW * TW));
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * D * NBW * (TW + 1)));
     asm volatile("s_barrier" ::: "memory");
 
     if (w_n > 0) {
@@ -301,16 +291,16 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_small_kernel(
       // zeros and touch no memory); an odd last batch runs on its own.
       int b = 0;
       for (; b + 1 < nbatch; b += 2) {
-        compute_batch(b, ta);
+        compute_batch(b, ta, sa);
         __builtin_amdgcn_sched_barrier(0);
-        load_batch(b + 2, ta);
+        load_batch(b + 2, ta, sa);
         __builtin_amdgcn_sched_barrier(0);
-        compute_batch(b + 1, tb);
+        compute_batch(b + 1, tb, sb);
         __builtin_amdgcn_sched_barrier(0);
-        load_batch(b + 3, tb);
+        load_batch(b + 3, tb, sb);
         __builtin_amdgcn_sched_barrier(0);
       }
-      if (b < nbatch) compute_batch(b, ta);
+      if (b < nbatch) compute_batch(b, ta, sa);
     }
   }
 
@@ -442,10 +432,11 @@ bool shape_supported(int nbw, int wn, int wk) {
   return false;
 }
 
-// LDS bytes per stage group: x fragments (rows padded to 16 unless M == 1)
-// and the scales of the workgroup's columns.
+// LDS bytes per staged group: x fragments, rows padded to 16 unless M == 1.
 int64_t lds_per_group(int wn, int nbw, int mr) {
-  return (mr == 1 ? 256 : 4096) + (int64_t)wn * nbw * 16 * 2;
+  (void)wn;
+  (void)nbw;
+  return mr == 1 ? 256 : 4096;
 }
 
 }  // namespace
