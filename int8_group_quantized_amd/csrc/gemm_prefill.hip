@@ -240,8 +240,11 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(2))) vo
 
 // Negated INT4 offsets: nbias[g * Mp + m] = -(136 * sum_{k in g} x[m, k]),
 // formed by the same 16x16x32 chain (four K steps of 32, from zero) that the
-// main kernel continues from. One wavefront per (16-row block, group); rows
-// from M to Mp repeat row M - 1.
+// main kernel continues from. One wavefront per (16-row block, run of
+// kBiasGroups groups), all of its x loads issued before the first multiply;
+// rows from M to Mp repeat row M - 1.
+constexpr int kBiasGroups = 4;
+
 __global__ __launch_bounds__(256) void prefill_bias_kernel(const uint16_t* __restrict__ x,
                                                            float* __restrict__ nbias, int M, int K,
                                                            int Mp, int units) {
@@ -249,17 +252,29 @@ __global__ __launch_bounds__(256) void prefill_bias_kernel(const uint16_t* __res
   const int u = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (u >= units) return;
   const int RB = Mp >> 4;
-  const int g = u / RB;
-  const int rb = u - g * RB;
+  const int G = K >> 7;
+  const int gc = u / RB;
+  const int rb = u - gc * RB;
   const int row = min(rb * 16 + (lane & 15), M - 1);
-  const uint16_t* src = x + (int64_t)row * K + g * kGroup + 8 * (lane >> 4);
-  const bf16x8 b136 = bias136_bf16x8();
-  f32x4 p = {0.f, 0.f, 0.f, 0.f};
+  const uint16_t* src = x + (int64_t)row * K + 8 * (lane >> 4);
+  bf16x8 a[kBiasGroups][4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    p = mfma16x16x32(*reinterpret_cast<const bf16x8*>(src + 32 * j), b136, p);
-  if ((lane & 15) == 0)
-    *reinterpret_cast<f32x4*>(nbias + (int64_t)g * Mp + rb * 16 + 4 * (lane >> 4)) = -p;
+  for (int i = 0; i < kBiasGroups; ++i) {
+    const int g = min(gc * kBiasGroups + i, G - 1);   // past G: re-read, not stored
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      a[i][j] = *reinterpret_cast<const bf16x8*>(src + g * kGroup + 32 * j);
+  }
+  const bf16x8 b136 = bias136_bf16x8();
+#pragma unroll
+  for (int i = 0; i < kBiasGroups; ++i) {
+    const int g = gc * kBiasGroups + i;
+    f32x4 p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) p = mfma16x16x32(a[i][j], b136, p);
+    if (g < G && (lane & 15) == 0)
+      *reinterpret_cast<f32x4*>(nbias + (int64_t)g * Mp + rb * 16 + 4 * (lane >> 4)) = -p;
+  }
 }
 
 template <int BITS, bool SBF, int WN, int NST>
@@ -324,7 +339,7 @@ hipError_t launch_gemm_prefill(int bits, const PrefillPlan& p, const void* x, co
   if (bits == 4) {
     // The offsets sit after the arrival counters, which stay untouched.
     float* nb = reinterpret_cast<float*>(static_cast<char*>(ws) + kCounterBytes);
-    const int units = (int)(p.mp / 16 * (K / kGroup));
+    const int units = (int)(p.mp / 16 * ((K / kGroup + kBiasGroups - 1) / kBiasGroups));
     prefill_bias_kernel<<<dim3((unsigned)((units + 3) / 4)), 256, 0, st>>>(xp, nb, m, k,
                                                                            (int)p.mp, units);
     if (s_bf16) launch_bits<4, true>(p, xp, wp, sp, nb, op, m, k, n, st);
