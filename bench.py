@@ -98,7 +98,7 @@ def alg_bytes(bits, M, K, N):
 class Weights:
     """Distinct device copies of one packed weight (RTN on the GPU)."""
 
-    def __init__(self, q, torch, cfg, shape_index, copies):
+    def __init__(self, q, torch, cfg, shape_index, copies, act="bf16"):
         import workloads
         w = workloads.WORKLOADS[cfg]
         self.bits, self.M = w["bits"], w["M"]
@@ -111,9 +111,10 @@ class Weights:
         self.copies = copies
         self.packed = [p] + [p.clone() for _ in range(copies - 1)]
         self.scales = [s] + [s.clone() for _ in range(copies - 1)]
-        xb = workloads.activations(self.M, self.K, workloads.seed_for(cfg, shape_index, 1))
-        self.x = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).cuda()
-        self.out = torch.empty((self.M, self.N), dtype=torch.bfloat16, device="cuda")
+        xb = workloads.activations(self.M, self.K, workloads.seed_for(cfg, shape_index, 1), dtype=act)
+        xdt = torch.bfloat16 if act == "bf16" else torch.float16
+        self.x = torch.from_numpy(xb.view(np.int16)).view(xdt).cuda()
+        self.out = torch.empty((self.M, self.N), dtype=xdt, device="cuda")
         self.ws = torch.zeros(max(q.workspace_bytes(self.bits, self.M, self.K, self.N), 1 << 16),
                               dtype=torch.uint8, device="cuda")
         self.bytes = alg_bytes(self.bits, self.M, self.K, self.N)
@@ -186,14 +187,14 @@ def kernel_average(torch, wt, q, launches=400):
     return ms / (100 * (launches // 100))
 
 
-def measure_workload(torch, q, cfg, reps=300):
+def measure_workload(torch, q, cfg, reps=300, act="bf16"):
     import workloads
     w = workloads.WORKLOADS[cfg]
     rows = []
     for si, (K, N) in enumerate(w["shapes"]):
         prefill = w["M"] > 16
         copies = 1 if prefill else copies_for(w["bits"], K, N)
-        wt = Weights(q, torch, cfg, si, copies)
+        wt = Weights(q, torch, cfg, si, copies, act=act)
         wt.W = None
         n = 4 if prefill else 100
         g = capture(torch, lambda i: wt.call(q, i), n)
@@ -213,7 +214,8 @@ def measure_workload(torch, q, cfg, reps=300):
         wt.free()
         del g
         torch.cuda.empty_cache()
-    return {"workload": w["name"], "shapes": rows}
+    name = w["name"] if act == "bf16" else w["name"].replace("a16", "a16_fp16act")
+    return {"workload": name, "shapes": rows}
 
 
 def measure_pack(torch, q):
@@ -236,6 +238,26 @@ def measure_pack(torch, q):
     nbytes = K * N * 4 + (K // 128) * N * 2 + K * N // 2
     gbs = nbytes / (ms * 1e-3) / 1e9
     return {"workload": "pack_to_grid_w4 fp32 W", "K": K, "N": N, "us_per_call": round(ms * 1e3, 2),
+            "gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+def measure_dequant(torch, q):
+    """Dense dequantization of the gate/up INT4 weight to bf16 (reads codes
+    and scales, writes 2 bytes per weight), over rotating weight copies."""
+    K, N = 2560, 19456
+    wt = Weights(q, torch, 2, 0, copies_for(4, K, N))
+    wt.W = None
+    dense = torch.empty((K, N), dtype=torch.bfloat16, device="cuda")
+    g = capture(torch, lambda i: q.dequant(wt.packed[i % wt.copies], wt.scales[i % wt.copies], 4,
+                                           K, N, out=dense), 20)
+    g.replay()
+    ms = time_graphs(torch, [g], reps=5) / 100
+    nbytes = K * N // 2 + (K // 128) * N * 2 + K * N * 2
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    wt.free()
+    del g, dense
+    torch.cuda.empty_cache()
+    return {"workload": "dequant_w4 -> bf16 dense", "K": K, "N": N, "us_per_call": round(ms * 1e3, 2),
             "gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
 
 
@@ -319,7 +341,9 @@ def main():
     if not args.only_headline:
         for cfg in (3, 4, 5):
             extra.append(measure_workload(torch, q, cfg))
+        extra.append(measure_workload(torch, q, 2, act="f16"))
         extra.append(measure_pack(torch, q))
+        extra.append(measure_dequant(torch, q))
 
     if args.copy_calibration:
         copy_calibration(torch)

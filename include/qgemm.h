@@ -18,7 +18,8 @@
  *
  * Conventions shared by every entry point
  *   - Logical layouts are row-major and contiguous:
- *       x[M,K] bf16, out[M,N] bf16, W[K,N], codes[K,N] int8,
+ *       x[M,K] bf16 (fp16 for the *f16 GEMMs), out[M,N] likewise,
+ *       W[K,N], codes[K,N] int8,
  *       scales[K/128, N] (fp16 or bf16).
  *     A PyTorch Linear weight is [N,K]; transpose it before packing.
  *   - K must be a positive multiple of 128 and N a positive multiple of 16,
@@ -82,13 +83,14 @@ size_t qg_packed_bytes(int bits, int64_t K, int64_t N);
 /* Bytes of the [K/128, N] scale array (2 bytes per scale). */
 size_t qg_scale_bytes(int64_t K, int64_t N);
 
-/* Workspace the GEMM needs for this shape (split-K partial sums and arrival
- * counters); 0 when the chosen plan needs none. The first 65536 bytes of a
- * workspace hold arrival counters: they must be zero before the first call
- * that uses the workspace, and every completed call leaves them zero again
- * (the rest holds fp32 partial sums and needs no initial value). Calls that
- * share one workspace must not overlap in time (use one stream or distinct
- * workspaces). */
+/* Workspace the GEMM needs for this shape; 0 when the chosen plan needs
+ * none. The first 65536 bytes of a workspace hold arrival counters: they must
+ * be zero before the first call that uses the workspace, and every completed
+ * call leaves them zero again. The rest holds fp32 split-K partial sums
+ * (M <= 16) or, for INT4 with M > 16, the per-row, per-group activation sums
+ * that remove the code offset; it needs no initial value. Calls that share
+ * one workspace must not overlap in time (use one stream or distinct
+ * workspaces). The same sizes apply to the fp16-activation entry points. */
 size_t qg_workspace_bytes(int bits, int64_t M, int64_t K, int64_t N);
 
 /* RTN scale choice from the weights, no calibration data (W8A16 model card:
@@ -138,8 +140,11 @@ qg_status qg_unpack_w8(const void* packed_w, int64_t K, int64_t N,
  *             see qg_workspace_bytes for the zero-counter rule.
  * Products of activations and codes are exact; each group of 128 is summed
  * in fp32, multiplied by its fp32 scale and added to an fp32 accumulator.
- * Supported domain: |x| < 1e30 (the int4 path carries a bias of 136 per
- * code through fp32 sums). */
+ * INT4 codes enter the product as 136 + q and the offset 136 * sum x of each
+ * group is removed in fp32: for M <= 16 both sums use the same instruction
+ * and order, so an all-zero code column gives exactly 0; for M > 16 the
+ * offset seeds the accumulation, leaving fp32 rounding of that cancellation.
+ * Supported domain: |x| < 1e30. */
 qg_status qgemm_w4a16(const void* x, const void* packed_w, const void* scales,
                       qg_dtype s_dt, void* out, int64_t M, int64_t K, int64_t N,
                       void* workspace, size_t workspace_bytes, void* stream);
@@ -167,6 +172,46 @@ qg_status qgemm_w8a16_plan(const void* x, const void* packed_w,
                            int k_waves, int splits, void* stream);
 size_t qg_workspace_bytes_plan(int bits, int64_t M, int64_t K, int64_t N,
                                int cols_per_wave, int k_waves, int splits);
+
+/* The W4A16 / W8A16 GEMMs with fp16 activations and fp16 output (the pages
+ * serve the target with INT4 weights and FP16 activations: adaptfm-quant-
+ * dflash README, "Stage 2: Target Model"; QAD paper, serving setup).
+ *   x    fp16 [M,K];  out  fp16 [M,N], fp32 -> fp16 round to nearest even
+ *        (values beyond the fp16 range become +-Inf).
+ * Everything else -- packed weights, scales, workspace, plans, errors -- is
+ * as for qgemm_w4a16 / qgemm_w8a16. INT4 codes enter as 1032 + q in fp16. */
+qg_status qgemm_w4f16(const void* x, const void* packed_w, const void* scales,
+                      qg_dtype s_dt, void* out, int64_t M, int64_t K, int64_t N,
+                      void* workspace, size_t workspace_bytes, void* stream);
+qg_status qgemm_w8f16(const void* x, const void* packed_w, const void* scales,
+                      qg_dtype s_dt, void* out, int64_t M, int64_t K, int64_t N,
+                      void* workspace, size_t workspace_bytes, void* stream);
+qg_status qgemm_w4f16_plan(const void* x, const void* packed_w,
+                           const void* scales, qg_dtype s_dt, void* out,
+                           int64_t M, int64_t K, int64_t N, void* workspace,
+                           size_t workspace_bytes, int cols_per_wave,
+                           int k_waves, int splits, void* stream);
+qg_status qgemm_w8f16_plan(const void* x, const void* packed_w,
+                           const void* scales, qg_dtype s_dt, void* out,
+                           int64_t M, int64_t K, int64_t N, void* workspace,
+                           size_t workspace_bytes, int cols_per_wave,
+                           int k_waves, int splits, void* stream);
+
+/* Dense dequantized weight W[k,n] = s[k/128, n] * q[k,n] (QAD paper, QAD
+ * paragraph: the student is initialised from the dequantized weights
+ * s (.) W_q; adaptfm-quant-dflash README, Stage 2: the dense dequantized
+ * bf16 twin used for drafter finetuning and calibration).
+ *   packed_w  qg_packed_bytes(bits,K,N) bytes
+ *   scales    [K/128,N]; s_dt = QG_F16 or QG_BF16
+ *   out       [K,N] row-major, out_dt = QG_BF16 or QG_F16
+ * s * q is exact in fp32; the one rounding is to out_dt, nearest even
+ * (+-Inf beyond its range). */
+qg_status qg_dequant_w4(const void* packed_w, const void* scales, qg_dtype s_dt,
+                        int64_t K, int64_t N, void* out, qg_dtype out_dt,
+                        void* stream);
+qg_status qg_dequant_w8(const void* packed_w, const void* scales, qg_dtype s_dt,
+                        int64_t K, int64_t N, void* out, qg_dtype out_dt,
+                        void* stream);
 
 #ifdef __cplusplus
 }

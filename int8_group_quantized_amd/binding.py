@@ -46,6 +46,14 @@ _SIGNATURES = {
                          _INT),
     "qgemm_w8a16_plan": ([_P, _P, _P, _INT, _P, _I64, _I64, _I64, _P, _SZ, _INT, _INT, _INT, _P],
                          _INT),
+    "qgemm_w4f16": ([_P, _P, _P, _INT, _P, _I64, _I64, _I64, _P, _SZ, _P], _INT),
+    "qgemm_w8f16": ([_P, _P, _P, _INT, _P, _I64, _I64, _I64, _P, _SZ, _P], _INT),
+    "qgemm_w4f16_plan": ([_P, _P, _P, _INT, _P, _I64, _I64, _I64, _P, _SZ, _INT, _INT, _INT, _P],
+                         _INT),
+    "qgemm_w8f16_plan": ([_P, _P, _P, _INT, _P, _I64, _I64, _I64, _P, _SZ, _INT, _INT, _INT, _P],
+                         _INT),
+    "qg_dequant_w4": ([_P, _P, _INT, _I64, _I64, _P, _INT, _P], _INT),
+    "qg_dequant_w8": ([_P, _P, _INT, _I64, _I64, _P, _INT, _P], _INT),
 }
 
 
@@ -181,27 +189,31 @@ def unpack(packed, K, N, bits):
 
 
 def qgemm(x, packed_w, scales, bits, N, out=None, plan=None, ws=None):
-    """out[M,N] = x[M,K] . (s (.) W_q) in bf16 with fp32 accumulation.
+    """out[M,N] = x[M,K] . (s (.) W_q) with fp32 accumulation; x and out are
+    both bf16 or both fp16 (qgemm_w*a16 / qgemm_w*f16 in the C ABI).
 
     plan: optional (cols_per_wave, k_waves, splits) for the small-M kernel.
     ws: optional workspace tensor (zeroed before first use).
     """
     _need_cuda(x, packed_w, scales, out)
-    if x.dtype != torch.bfloat16:
-        raise TypeError("x must be bf16")
+    if x.dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError("x must be bf16 or fp16")
+    act = "a16" if x.dtype == torch.bfloat16 else "f16"
     M, K = x.shape
     if out is None:
-        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+        out = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    elif out.dtype != x.dtype:
+        raise TypeError("out must have the dtype of x")
     need = workspace_bytes(bits, M, K, N, plan)
     if ws is None and need > 0:
         ws = workspace(x.device, need)
     ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
     if plan is None:
-        fn = "qgemm_w%da16" % bits
+        fn = "qgemm_w%d%s" % (bits, act)
         code = getattr(lib(), fn)(_ptr(x), _ptr(packed_w), _ptr(scales), _dt(scales), _ptr(out),
                                   M, K, N, _ptr(ws), ws_bytes, _stream(x))
     else:
-        fn = "qgemm_w%da16_plan" % bits
+        fn = "qgemm_w%d%s_plan" % (bits, act)
         code = getattr(lib(), fn)(_ptr(x), _ptr(packed_w), _ptr(scales), _dt(scales), _ptr(out),
                                   M, K, N, _ptr(ws), ws_bytes, plan[0], plan[1], plan[2],
                                   _stream(x))
@@ -215,3 +227,14 @@ def qgemm_w4a16(x, packed_w, scales, N, out=None, plan=None, ws=None):
 
 def qgemm_w8a16(x, packed_w, scales, N, out=None, plan=None, ws=None):
     return qgemm(x, packed_w, scales, 8, N, out=out, plan=plan, ws=ws)
+
+
+def dequant(packed_w, scales, bits, K, N, dtype=torch.bfloat16, out=None):
+    """Dense W[K,N] = s (.) W_q, rounded once to dtype (bf16 or fp16)."""
+    _need_cuda(packed_w, scales, out)
+    if out is None:
+        out = torch.empty((K, N), dtype=dtype, device=packed_w.device)
+    fn = "qg_dequant_w%d" % bits
+    _check(fn, getattr(lib(), fn)(_ptr(packed_w), _ptr(scales), _dt(scales), K, N, _ptr(out),
+                                  _dt(out), _stream(packed_w)))
+    return out

@@ -77,9 +77,9 @@ qg_status unpack(int bits, const void* packed, int64_t K, int64_t N, int8_t* cod
   return from_hip(qg::launch_unpack(bits, packed, K, N, codes, as_stream(stream)));
 }
 
-qg_status gemm(int bits, const void* x, const void* packed, const void* scales, qg_dtype s_dt,
-               void* out, int64_t M, int64_t K, int64_t N, void* ws, size_t ws_bytes, int nbw,
-               int wk, int splits, void* stream) {
+qg_status gemm(int bits, bool x_f16, const void* x, const void* packed, const void* scales,
+               qg_dtype s_dt, void* out, int64_t M, int64_t K, int64_t N, void* ws,
+               size_t ws_bytes, int nbw, int wk, int splits, void* stream) {
   qg_status s = check_mkn(M, K, N);
   if (s != QG_OK) return s;
   if (s_dt != QG_F16 && s_dt != QG_BF16) return QG_ERR_DTYPE;
@@ -95,8 +95,8 @@ qg_status gemm(int bits, const void* x, const void* packed, const void* scales, 
       if (ws == nullptr || ws_bytes < need) return QG_ERR_WORKSPACE;
       if (!aligned16(ws)) return QG_ERR_ALIGN;
     }
-    return from_hip(qg::launch_gemm_prefill(bits, pp, x, packed, scales, s_dt == QG_BF16, out,
-                                            M, K, N, ws, as_stream(stream)));
+    return from_hip(qg::launch_gemm_prefill(bits, pp, x, x_f16, packed, scales, s_dt == QG_BF16,
+                                            out, M, K, N, ws, as_stream(stream)));
   }
   qg::SmallPlan plan;
   if (!qg::make_small_plan(bits, M, K, N, nbw, wk, splits, &plan)) return QG_ERR_PLAN;
@@ -105,8 +105,19 @@ qg_status gemm(int bits, const void* x, const void* packed, const void* scales, 
     if (ws == nullptr || ws_bytes < need) return QG_ERR_WORKSPACE;
     if (!aligned16(ws)) return QG_ERR_ALIGN;
   }
-  return from_hip(qg::launch_gemm_small(bits, plan, x, packed, scales, s_dt == QG_BF16, out, M, K,
-                                        N, ws, as_stream(stream)));
+  return from_hip(qg::launch_gemm_small(bits, plan, x, x_f16, packed, scales, s_dt == QG_BF16,
+                                        out, M, K, N, ws, as_stream(stream)));
+}
+
+qg_status dequant(int bits, const void* packed, const void* scales, qg_dtype s_dt, int64_t K,
+                  int64_t N, void* out, qg_dtype out_dt, void* stream) {
+  qg_status s = check_kn(K, N);
+  if (s != QG_OK) return s;
+  if (s_dt != QG_F16 && s_dt != QG_BF16) return QG_ERR_DTYPE;
+  if (out_dt != QG_F16 && out_dt != QG_BF16) return QG_ERR_DTYPE;
+  if ((s = check_ptrs({packed, scales, out})) != QG_OK) return s;
+  return from_hip(qg::launch_dequant(bits, packed, scales, s_dt == QG_BF16, out, out_dt == QG_F16,
+                                     K, N, as_stream(stream)));
 }
 
 size_t workspace_bytes(int bits, int64_t M, int64_t K, int64_t N, int nbw, int wk, int splits) {
@@ -199,22 +210,22 @@ qg_status qg_unpack_w8(const void* packed_w, int64_t K, int64_t N, int8_t* codes
 qg_status qgemm_w4a16(const void* x, const void* packed_w, const void* scales, qg_dtype s_dt,
                       void* out, int64_t M, int64_t K, int64_t N, void* workspace,
                       size_t workspace_bytes, void* stream) {
-  return gemm(4, x, packed_w, scales, s_dt, out, M, K, N, workspace, workspace_bytes, 0, 0, 0,
-              stream);
+  return gemm(4, false, x, packed_w, scales, s_dt, out, M, K, N, workspace, workspace_bytes, 0,
+              0, 0, stream);
 }
 
 qg_status qgemm_w8a16(const void* x, const void* packed_w, const void* scales, qg_dtype s_dt,
                       void* out, int64_t M, int64_t K, int64_t N, void* workspace,
                       size_t workspace_bytes, void* stream) {
-  return gemm(8, x, packed_w, scales, s_dt, out, M, K, N, workspace, workspace_bytes, 0, 0, 0,
-              stream);
+  return gemm(8, false, x, packed_w, scales, s_dt, out, M, K, N, workspace, workspace_bytes, 0,
+              0, 0, stream);
 }
 
 qg_status qgemm_w4a16_plan(const void* x, const void* packed_w, const void* scales, qg_dtype s_dt,
                            void* out, int64_t M, int64_t K, int64_t N, void* workspace,
                            size_t workspace_bytes, int cols_per_wave, int k_waves, int splits,
                            void* stream) {
-  return gemm(4, x, packed_w, scales, s_dt, out, M, K, N, workspace, workspace_bytes,
+  return gemm(4, false, x, packed_w, scales, s_dt, out, M, K, N, workspace, workspace_bytes,
               cols_per_wave, k_waves, splits, stream);
 }
 
@@ -222,8 +233,48 @@ qg_status qgemm_w8a16_plan(const void* x, const void* packed_w, const void* scal
                            void* out, int64_t M, int64_t K, int64_t N, void* workspace,
                            size_t workspace_bytes, int cols_per_wave, int k_waves, int splits,
                            void* stream) {
-  return gemm(8, x, packed_w, scales, s_dt, out, M, K, N, workspace, workspace_bytes,
+  return gemm(8, false, x, packed_w, scales, s_dt, out, M, K, N, workspace, workspace_bytes,
               cols_per_wave, k_waves, splits, stream);
+}
+
+qg_status qgemm_w4f16(const void* x, const void* packed_w, const void* scales, qg_dtype s_dt,
+                      void* out, int64_t M, int64_t K, int64_t N, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  return gemm(4, true, x, packed_w, scales, s_dt, out, M, K, N, workspace, workspace_bytes, 0, 0,
+              0, stream);
+}
+
+qg_status qgemm_w8f16(const void* x, const void* packed_w, const void* scales, qg_dtype s_dt,
+                      void* out, int64_t M, int64_t K, int64_t N, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  return gemm(8, true, x, packed_w, scales, s_dt, out, M, K, N, workspace, workspace_bytes, 0, 0,
+              0, stream);
+}
+
+qg_status qgemm_w4f16_plan(const void* x, const void* packed_w, const void* scales, qg_dtype s_dt,
+                           void* out, int64_t M, int64_t K, int64_t N, void* workspace,
+                           size_t workspace_bytes, int cols_per_wave, int k_waves, int splits,
+                           void* stream) {
+  return gemm(4, true, x, packed_w, scales, s_dt, out, M, K, N, workspace, workspace_bytes,
+              cols_per_wave, k_waves, splits, stream);
+}
+
+qg_status qgemm_w8f16_plan(const void* x, const void* packed_w, const void* scales, qg_dtype s_dt,
+                           void* out, int64_t M, int64_t K, int64_t N, void* workspace,
+                           size_t workspace_bytes, int cols_per_wave, int k_waves, int splits,
+                           void* stream) {
+  return gemm(8, true, x, packed_w, scales, s_dt, out, M, K, N, workspace, workspace_bytes,
+              cols_per_wave, k_waves, splits, stream);
+}
+
+qg_status qg_dequant_w4(const void* packed_w, const void* scales, qg_dtype s_dt, int64_t K,
+                        int64_t N, void* out, qg_dtype out_dt, void* stream) {
+  return dequant(4, packed_w, scales, s_dt, K, N, out, out_dt, stream);
+}
+
+qg_status qg_dequant_w8(const void* packed_w, const void* scales, qg_dtype s_dt, int64_t K,
+                        int64_t N, void* out, qg_dtype out_dt, void* stream) {
+  return dequant(8, packed_w, scales, s_dt, K, N, out, out_dt, stream);
 }
 
 }  // extern "C"

@@ -57,16 +57,9 @@ __device__ __forceinline__ void to_lds(const void* src, char* dst) {
   __builtin_amdgcn_global_load_lds(src, (lds_ptr)dst, 16, 0, 0);
 }
 
-__device__ __forceinline__ bf16x8 int4_to_biased(uint32_t w, uint32_t magic) {
-  const u32x4 r = {(w & 0x000F000Fu) | magic, ((w >> 4) & 0x000F000Fu) | magic,
-                   ((w >> 8) & 0x000F000Fu) | magic, ((w >> 12) & 0x000F000Fu) | magic};
-  return __builtin_bit_cast(bf16x8, r);
-}
-
-// The magic lives in a VGPR so that the and-or takes the mask as its one
-// scalar operand.
-__device__ __forceinline__ uint32_t opaque_bias_magic() {
-  uint32_t m = 0x43004300u;
+// The INT4 expansion constant in a vector register (so the mask takes the
+// one scalar slot of the AND-OR); the empty asm emits no instruction.
+__device__ __forceinline__ uint32_t opaque_magic(uint32_t m) {
   asm volatile("" : "+v"(m));
   return m;
 }
@@ -112,12 +105,13 @@ __device__ __forceinline__ void load_stage(char* st, const uint16_t* __restrict_
   }
 }
 
-template <int BITS, bool SBF, int WN, int NST>
+template <int BITS, bool SBF, bool XH, int WN, int NST>
 __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(2))) void gemm_prefill_kernel(
     const uint16_t* __restrict__ x, const char* __restrict__ packed,
     const uint16_t* __restrict__ scales, const float* __restrict__ nbias,
     uint16_t* __restrict__ out, int M, int K, int N, int Mp, int tiles_n, int tiles) {
   using S = Stage<BITS, WN, NST>;
+  using A = Act<XH>;
   extern __shared__ u32x4 smem[];
   char* const lds = reinterpret_cast<char*>(smem);
 
@@ -138,7 +132,7 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(2))) vo
   const int m0 = tm * kBM;
   const int cb0 = tn * 4 * WN;
 
-  const uint32_t magic = opaque_bias_magic();
+  const uint32_t magic = opaque_magic(A::kMagic);
 
   f32x4 acc[4][4];   // [column block][row block]
 #pragma unroll
@@ -171,12 +165,12 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(2))) vo
     const char* st = lds + cur * S::kBytes;
     cur = (cur == NST - 1) ? 0 : cur + 1;
 
-    bf16x8 a[4][4];
+    u32x4 a[4][4];
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        a[r][j] = *reinterpret_cast<const bf16x8*>(st + (r * 4 + j) * 1024 + lane * 16);
+        a[r][j] = *reinterpret_cast<const u32x4*>(st + (r * 4 + j) * 1024 + lane * 16);
     f32x4 seed[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -195,26 +189,26 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(2))) vo
 
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      bf16x8 bw[4];
+      u32x4 bw[4];
       if constexpr (BITS == 4) {
         const u32x4 w = *reinterpret_cast<const u32x4*>(st + S::kB + (wave * 4 + c) * 1024 + lane * 16);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) bw[j] = int4_to_biased(w[j], magic);
+        for (int j = 0; j < 4; ++j) bw[j] = int4_word_to_act(w[j], magic);
       } else {
         const char* tp = st + S::kB + (wave * 4 + c) * 2048 + lane * 32;
         const u32x4 w0 = *reinterpret_cast<const u32x4*>(tp);
         const u32x4 w1 = *reinterpret_cast<const u32x4*>(tp + 16);
-        bw[0] = int8_words_to_bf16(w0[0], w0[1]);
-        bw[1] = int8_words_to_bf16(w0[2], w0[3]);
-        bw[2] = int8_words_to_bf16(w1[0], w1[1]);
-        bw[3] = int8_words_to_bf16(w1[2], w1[3]);
+        bw[0] = int8_words_to_act<A>(w0[0], w0[1]);
+        bw[1] = int8_words_to_act<A>(w0[2], w0[3]);
+        bw[2] = int8_words_to_act<A>(w1[0], w1[1]);
+        bw[3] = int8_words_to_act<A>(w1[2], w1[3]);
       }
       const float s = SBF ? bf16_bits_to_f32(sraw[c]) : f16_bits_to_f32(sraw[c]);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         f32x4 p = seed[r];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) p = mfma16x16x32(a[r][j], bw[j], p);
+        for (int j = 0; j < 4; ++j) p = A::mma(a[r][j], bw[j], p);
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[c][r][e] = fmaf(s, p[e], acc[c][r][e]);
       }
@@ -232,19 +226,21 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int row = m0 + r * 16 + 4 * lq + e;
-        if (row < M) out[(int64_t)row * N + n] = f32_to_bf16_bits(acc[c][r][e]);
+        if (row < M) out[(int64_t)row * N + n] = A::out(acc[c][r][e]);
       }
     }
   }
 }
 
-// Negated INT4 offsets: nbias[g * Mp + m] = -(136 * sum_{k in g} x[m, k]),
+// Negated INT4 offsets: nbias[g * Mp + m] = -(c * sum_{k in g} x[m, k]) with
+// c = 136 (bf16 activations) or 1032 (fp16),
 // formed by the same 16x16x32 chain (four K steps of 32, from zero) that the
 // main kernel continues from. One wavefront per (16-row block, run of
 // kBiasGroups groups), all of its x loads issued before the first multiply;
 // rows from M to Mp repeat row M - 1.
 constexpr int kBiasGroups = 4;
 
+template <bool XH>
 __global__ __launch_bounds__(256) void prefill_bias_kernel(const uint16_t* __restrict__ x,
                                                            float* __restrict__ nbias, int M, int K,
                                                            int Mp, int units) {
@@ -257,39 +253,40 @@ __global__ __launch_bounds__(256) void prefill_bias_kernel(const uint16_t* __res
   const int rb = u - gc * RB;
   const int row = min(rb * 16 + (lane & 15), M - 1);
   const uint16_t* src = x + (int64_t)row * K + 8 * (lane >> 4);
-  bf16x8 a[kBiasGroups][4];
+  using A = Act<XH>;
+  u32x4 a[kBiasGroups][4];
 #pragma unroll
   for (int i = 0; i < kBiasGroups; ++i) {
     const int g = min(gc * kBiasGroups + i, G - 1);   // past G: re-read, not stored
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      a[i][j] = *reinterpret_cast<const bf16x8*>(src + g * kGroup + 32 * j);
+      a[i][j] = *reinterpret_cast<const u32x4*>(src + g * kGroup + 32 * j);
   }
-  const bf16x8 b136 = bias136_bf16x8();
+  const u32x4 off = {A::kOffset, A::kOffset, A::kOffset, A::kOffset};
 #pragma unroll
   for (int i = 0; i < kBiasGroups; ++i) {
     const int g = gc * kBiasGroups + i;
     f32x4 p = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) p = mfma16x16x32(a[i][j], b136, p);
+    for (int j = 0; j < 4; ++j) p = A::mma(a[i][j], off, p);
     if (g < G && (lane & 15) == 0)
       *reinterpret_cast<f32x4*>(nbias + (int64_t)g * Mp + rb * 16 + 4 * (lane >> 4)) = -p;
   }
 }
 
-template <int BITS, bool SBF, int WN, int NST>
+template <int BITS, bool SBF, bool XH, int WN, int NST>
 void launch_main(const PrefillPlan& p, const uint16_t* x, const char* w, const uint16_t* s,
                  const float* nb, uint16_t* out, int M, int K, int N, hipStream_t st) {
-  gemm_prefill_kernel<BITS, SBF, WN, NST>
+  gemm_prefill_kernel<BITS, SBF, XH, WN, NST>
       <<<dim3((unsigned)p.tiles), 64 * WN, NST * Stage<BITS, WN, NST>::kBytes, st>>>(
           x, w, s, nb, out, M, K, N, (int)p.mp, p.tiles_n, p.tiles);
 }
 
-template <int BITS, bool SBF>
+template <int BITS, bool SBF, bool XH>
 void launch_bits(const PrefillPlan& p, const uint16_t* x, const char* w, const uint16_t* s,
                  const float* nb, uint16_t* out, int M, int K, int N, hipStream_t st) {
-  if (p.wn == 4) launch_main<BITS, SBF, 4, 2>(p, x, w, s, nb, out, M, K, N, st);
-  else           launch_main<BITS, SBF, 2, 2>(p, x, w, s, nb, out, M, K, N, st);
+  if (p.wn == 4) launch_main<BITS, SBF, XH, 4, 2>(p, x, w, s, nb, out, M, K, N, st);
+  else           launch_main<BITS, SBF, XH, 2, 2>(p, x, w, s, nb, out, M, K, N, st);
 }
 
 constexpr int kCUs = 256;   // MI355X compute units (plan heuristic only)
@@ -328,9 +325,9 @@ size_t prefill_workspace(int bits, const PrefillPlan& p, int64_t K) {
   return (size_t)kCounterBytes + (size_t)p.mp * (size_t)(K / kGroup) * sizeof(float);
 }
 
-hipError_t launch_gemm_prefill(int bits, const PrefillPlan& p, const void* x, const void* packed,
-                               const void* scales, bool s_bf16, void* out, int64_t M, int64_t K,
-                               int64_t N, void* ws, hipStream_t st) {
+hipError_t launch_gemm_prefill(int bits, const PrefillPlan& p, const void* x, bool x_f16,
+                               const void* packed, const void* scales, bool s_bf16, void* out,
+                               int64_t M, int64_t K, int64_t N, void* ws, hipStream_t st) {
   const auto* xp = static_cast<const uint16_t*>(x);
   const auto* wp = static_cast<const char*>(packed);
   const auto* sp = static_cast<const uint16_t*>(scales);
@@ -340,13 +337,24 @@ hipError_t launch_gemm_prefill(int bits, const PrefillPlan& p, const void* x, co
     // The offsets sit after the arrival counters, which stay untouched.
     float* nb = reinterpret_cast<float*>(static_cast<char*>(ws) + kCounterBytes);
     const int units = (int)(p.mp / 16 * ((K / kGroup + kBiasGroups - 1) / kBiasGroups));
-    prefill_bias_kernel<<<dim3((unsigned)((units + 3) / 4)), 256, 0, st>>>(xp, nb, m, k,
-                                                                           (int)p.mp, units);
-    if (s_bf16) launch_bits<4, true>(p, xp, wp, sp, nb, op, m, k, n, st);
-    else        launch_bits<4, false>(p, xp, wp, sp, nb, op, m, k, n, st);
+    const dim3 bgrid((unsigned)((units + 3) / 4));
+    if (x_f16) prefill_bias_kernel<true><<<bgrid, 256, 0, st>>>(xp, nb, m, k, (int)p.mp, units);
+    else       prefill_bias_kernel<false><<<bgrid, 256, 0, st>>>(xp, nb, m, k, (int)p.mp, units);
+    if (x_f16) {
+      if (s_bf16) launch_bits<4, true, true>(p, xp, wp, sp, nb, op, m, k, n, st);
+      else        launch_bits<4, false, true>(p, xp, wp, sp, nb, op, m, k, n, st);
+    } else {
+      if (s_bf16) launch_bits<4, true, false>(p, xp, wp, sp, nb, op, m, k, n, st);
+      else        launch_bits<4, false, false>(p, xp, wp, sp, nb, op, m, k, n, st);
+    }
   } else {
-    if (s_bf16) launch_bits<8, true>(p, xp, wp, sp, nullptr, op, m, k, n, st);
-    else        launch_bits<8, false>(p, xp, wp, sp, nullptr, op, m, k, n, st);
+    if (x_f16) {
+      if (s_bf16) launch_bits<8, true, true>(p, xp, wp, sp, nullptr, op, m, k, n, st);
+      else        launch_bits<8, false, true>(p, xp, wp, sp, nullptr, op, m, k, n, st);
+    } else {
+      if (s_bf16) launch_bits<8, true, false>(p, xp, wp, sp, nullptr, op, m, k, n, st);
+      else        launch_bits<8, false, false>(p, xp, wp, sp, nullptr, op, m, k, n, st);
+    }
   }
   return hipGetLastError();
 }

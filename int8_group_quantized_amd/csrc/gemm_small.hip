@@ -65,22 +65,11 @@ __device__ __forceinline__ float load_coherent(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// INT4 word (nibble p holds element p/2 + 4*(p%2), value q + 8) -> eight
-// bf16 values 128 + u in element order: (w >> 4i) & 0x000F000F | magic per
-// pair. `magic` must arrive as an opaque vector-register value (see
-// opaque_magic) so the compiler selects one AND-OR per pair: a three-operand
-// vector op may read only one scalar or constant operand, and the mask takes
-// that slot.
-__device__ __forceinline__ bf16x8 int4_word_to_biased(uint32_t w, uint32_t magic) {
-  const u32x4 r = {(w & 0x000F000Fu) | magic, ((w >> 4) & 0x000F000Fu) | magic,
-                   ((w >> 8) & 0x000F000Fu) | magic, ((w >> 12) & 0x000F000Fu) | magic};
-  return __builtin_bit_cast(bf16x8, r);
-}
-
-// 0x43004300 (two bf16 128.0) held in a vector register the optimiser
-// cannot fold back into a literal. The empty asm emits no instruction.
-__device__ __forceinline__ uint32_t opaque_magic() {
-  uint32_t m = 0x43004300u;
+// The INT4 expansion constant held in a vector register the optimiser cannot
+// fold back into a literal, so the compiler selects one AND-OR per pair (a
+// three-operand vector op may read only one scalar or constant operand, and
+// the mask takes that slot). The empty asm emits no instruction.
+__device__ __forceinline__ uint32_t opaque_magic(uint32_t m) {
   asm volatile("" : "+v"(m));
   return m;
 }
@@ -113,7 +102,7 @@ struct Batch {
                                        : (NBW == 1 ? 2 : 1);
 };
 
-template <int BITS, bool SBF, int MR, int NBW, int WN, int WK>
+template <int BITS, bool SBF, bool XH, int MR, int NBW, int WN, int WK>
 __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_small_kernel(
     const uint16_t* __restrict__ x, const char* packed, const uint16_t* scales,
     uint16_t* __restrict__ out,
@@ -125,6 +114,7 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_small_kernel(
   constexpr int TW = Tile<BITS>::words;
   constexpr int D = Batch<BITS, NBW>::D;
   constexpr int XG = (MR == 1) ? 16 : 256;   // LDS 16-byte words of x per group
+  using A = Act<XH>;
   extern __shared__ u32x4 smem[];
 
   const int tid = threadIdx.x;
@@ -144,7 +134,7 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_small_kernel(
   const int l16 = lane & 15;                 // A row / C column of this lane
   const int lq = lane >> 4;                  // K slice (A, B) / row quad (C)
   u32x4* xs = smem;                          // [sg][XG] x fragments, then a zero block (MR == 1)
-  const uint32_t magic = opaque_magic();
+  const uint32_t magic = opaque_magic(A::kMagic);
 
   int cb[NBW];
 #pragma unroll
@@ -203,14 +193,14 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_small_kernel(
         const bool live = i < w_n;
         const int gl = w_lo + min(i, w_n - 1);        // stage-relative group
         const u32x4* xp = xs + xa_lane + gl * xa_step;
-        bf16x8 a[4];
+        u32x4 a[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) a[j] = __builtin_bit_cast(bf16x8, xp[j * (XG / 4)]);
+        for (int j = 0; j < 4; ++j) a[j] = xp[j * (XG / 4)];
         f32x4 bias = {0.f, 0.f, 0.f, 0.f};
         if constexpr (BITS == 4) {
-          const bf16x8 b136 = bias136_bf16x8();
+          const u32x4 off = {A::kOffset, A::kOffset, A::kOffset, A::kOffset};
 #pragma unroll
-          for (int j = 0; j < 4; ++j) bias = mfma16x16x32(a[j], b136, bias);
+          for (int j = 0; j < 4; ++j) bias = A::mma(a[j], off, bias);
         }
 #pragma unroll
         for (int c = 0; c < NBW; ++c) {
@@ -218,12 +208,12 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_small_kernel(
           if constexpr (BITS == 4) {
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-              p = mfma16x16x32(a[j], int4_word_to_biased(t[d][c][0][j], magic), p);
+              p = A::mma(a[j], int4_word_to_act(t[d][c][0][j], magic), p);
           } else {
-            p = mfma16x16x32(a[0], int8_words_to_bf16(t[d][c][0][0], t[d][c][0][1]), p);
-            p = mfma16x16x32(a[1], int8_words_to_bf16(t[d][c][0][2], t[d][c][0][3]), p);
-            p = mfma16x16x32(a[2], int8_words_to_bf16(t[d][c][1][0], t[d][c][1][1]), p);
-            p = mfma16x16x32(a[3], int8_words_to_bf16(t[d][c][1][2], t[d][c][1][3]), p);
+            p = A::mma(a[0], int8_words_to_act<A>(t[d][c][0][0], t[d][c][0][1]), p);
+            p = A::mma(a[1], int8_words_to_act<A>(t[d][c][0][2], t[d][c][0][3]), p);
+            p = A::mma(a[2], int8_words_to_act<A>(t[d][c][1][0], t[d][c][1][1]), p);
+            p = A::mma(a[3], int8_words_to_act<A>(t[d][c][1][2], t[d][c][1][3]), p);
           }
           const uint32_t sbits = sc[d][c];
           const float sv = SBF ? bf16_bits_to_f32(sbits) : f16_bits_to_f32(sbits);
@@ -336,7 +326,7 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_small_kernel(
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * lq + e;
-            if (r < mrows) out[(int64_t)(row0 + r) * N + n] = f32_to_bf16_bits(acc[c][e]);
+            if (r < mrows) out[(int64_t)(row0 + r) * N + n] = A::out(acc[c][e]);
           }
         }
       }
@@ -382,7 +372,7 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_small_kernel(
             float sum = 0.0f;
             for (int sp = 0; sp < splits; ++sp)
               sum += load_coherent(&partials[((int64_t)sp * M + row0 + r) * N + n]);
-            out[(int64_t)(row0 + r) * N + n] = f32_to_bf16_bits(sum);
+            out[(int64_t)(row0 + r) * N + n] = A::out(sum);
           }
         }
       }
@@ -392,7 +382,7 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_small_kernel(
     __hip_atomic_store(&counters[cidx], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int BITS, bool SBF, int MR, int NBW, int WN, int WK>
+template <int BITS, bool SBF, bool XH, int MR, int NBW, int WN, int WK>
 hipError_t launch_variant(const SmallPlan& p, const void* x, const void* packed,
                           const void* scales, void* out, int64_t M, int64_t K, int64_t N,
                           void* ws, hipStream_t st) {
@@ -404,19 +394,19 @@ hipError_t launch_variant(const SmallPlan& p, const void* x, const void* packed,
     partials = reinterpret_cast<float*>(static_cast<char*>(ws) + kCounterBytes);
   }
   const size_t lds = small_plan_lds_bytes(p, M);
-  gemm_small_kernel<BITS, SBF, MR, NBW, WN, WK><<<grid, 64 * WN * WK, lds, st>>>(
+  gemm_small_kernel<BITS, SBF, XH, MR, NBW, WN, WK><<<grid, 64 * WN * WK, lds, st>>>(
       static_cast<const uint16_t*>(x), static_cast<const char*>(packed),
       static_cast<const uint16_t*>(scales), static_cast<uint16_t*>(out), counters, partials,
       (int)M, (int)K, (int)N, p.splits, p.gps, p.sg);
   return hipGetLastError();
 }
 
-template <int BITS, bool SBF, int MR>
+template <int BITS, bool SBF, bool XH, int MR>
 hipError_t launch_shape(const SmallPlan& p, const void* x, const void* packed, const void* scales,
                         void* out, int64_t M, int64_t K, int64_t N, void* ws, hipStream_t st) {
 #define QG_V(NBW, WN, WK)                                                                    \
   if (p.nbw == NBW && p.wn == WN && p.wk == WK)                                              \
-    return launch_variant<BITS, SBF, MR, NBW, WN, WK>(p, x, packed, scales, out, M, K, N, ws, st);
+    return launch_variant<BITS, SBF, XH, MR, NBW, WN, WK>(p, x, packed, scales, out, M, K, N, ws, st);
   QG_V(1, 4, 1) QG_V(1, 2, 2) QG_V(1, 1, 4) QG_V(1, 1, 8)
   QG_V(2, 4, 1) QG_V(2, 1, 4)
   QG_V(4, 4, 1) QG_V(4, 1, 4)
@@ -515,14 +505,16 @@ size_t small_plan_workspace(const SmallPlan& p, int64_t M, int64_t N) {
   return (size_t)kCounterBytes + (size_t)p.splits * (size_t)M * (size_t)N * sizeof(float);
 }
 
-hipError_t launch_gemm_small(int bits, const SmallPlan& p, const void* x, const void* packed,
-                             const void* scales, bool s_bf16, void* out, int64_t M, int64_t K,
-                             int64_t N, void* ws, hipStream_t st) {
-#define QG_B(B, S, R)                                                                     \
-  if (bits == B && s_bf16 == S && p.mr == R)                                              \
-    return launch_shape<B, S, R>(p, x, packed, scales, out, M, K, N, ws, st);
-  QG_B(4, false, 1) QG_B(4, false, 16) QG_B(4, true, 1) QG_B(4, true, 16)
-  QG_B(8, false, 1) QG_B(8, false, 16) QG_B(8, true, 1) QG_B(8, true, 16)
+hipError_t launch_gemm_small(int bits, const SmallPlan& p, const void* x, bool x_f16,
+                             const void* packed, const void* scales, bool s_bf16, void* out,
+                             int64_t M, int64_t K, int64_t N, void* ws, hipStream_t st) {
+#define QG_B(B, S, H, R)                                                                  \
+  if (bits == B && s_bf16 == S && x_f16 == H && p.mr == R)                                \
+    return launch_shape<B, S, H, R>(p, x, packed, scales, out, M, K, N, ws, st);
+  QG_B(4, false, false, 1) QG_B(4, false, false, 16) QG_B(4, true, false, 1) QG_B(4, true, false, 16)
+  QG_B(8, false, false, 1) QG_B(8, false, false, 16) QG_B(8, true, false, 1) QG_B(8, true, false, 16)
+  QG_B(4, false, true, 1) QG_B(4, false, true, 16) QG_B(4, true, true, 1) QG_B(4, true, true, 16)
+  QG_B(8, false, true, 1) QG_B(8, false, true, 16) QG_B(8, true, true, 1) QG_B(8, true, true, 16)
 #undef QG_B
   return hipErrorInvalidValue;
 }

@@ -5,6 +5,10 @@
 //                  (arXiv 2607.04244, QAD paragraph: updated bf16 weights
 //                  rounded back onto the frozen grid)
 //   prepack/unpack reorder logical codes into / out of the packed tiles
+//   dequant        the dense weight s (.) W_q in bf16 or fp16
+//                  (arXiv 2607.04244, QAD paragraph: the student starts from
+//                  the dequantized weights; README "Stage 2": the dense
+//                  dequantized twin used for finetuning and calibration)
 //
 // Thread mapping for the tile kernels: one thread per (tile, lane), i.e. per
 // 16 packed bytes (INT4) or 32 (INT8). A thread's 32 codes share one column
@@ -169,6 +173,80 @@ __global__ __launch_bounds__(256) void unpack_kernel(const void* __restrict__ pa
   }
 }
 
+// Dense dequantization: out[k, n] = round(s[g, n] * q[k, n]) in bf16 or fp16
+// (OH), k in group g. The product of the decoded scale and the integer code
+// is exact in fp32 (at most 11 + 8 significant bits), so the one rounding is
+// the RNE conversion to the output format. A workgroup takes one group and
+// eight column blocks (128 x 128 outputs): each wavefront expands two tiles
+// into an LDS block, then the workgroup writes whole 256-byte row segments.
+constexpr int kDqCols = 128;                 // columns per workgroup
+constexpr int kDqStride = kDqCols + 8;       // LDS row stride (16-bit), spreads banks
+
+template <int BITS, bool SBF, bool OH>
+__global__ __launch_bounds__(256) void dequant_kernel(const void* __restrict__ packed,
+                                                      const uint16_t* __restrict__ scales,
+                                                      uint16_t* __restrict__ out, int K, int N) {
+  __shared__ uint16_t blk[kGroup * kDqStride];
+  constexpr int TB = (BITS == 4) ? 1024 : 2048;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int l16 = lane & 15;
+  const int lq = lane >> 4;
+  const int G = K / kGroup;
+  const int NB = N / kTileCols;
+  const int g = blockIdx.y;
+  const int cb0 = blockIdx.x * (kDqCols / kTileCols);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int cbl = wave * 2 + h;
+    const int cb = cb0 + cbl;
+    if (cb >= NB) break;
+    const char* tp = static_cast<const char*>(packed) + ((int64_t)cb * G + g) * TB + lane * (TB / 64);
+    const uint32_t sb = scales[(int64_t)g * N + cb * 16 + l16];
+    const float s = SBF ? bf16_bits_to_f32(sb) : f16_bits_to_f32(sb);
+    int q[32];
+    if constexpr (BITS == 4) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(tp);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[8 * j + i] = (int)((w[j] >> (4 * nibble_of(i))) & 15u) - 8;
+    } else {
+      const u32x4 a = reinterpret_cast<const u32x4*>(tp)[0], b = reinterpret_cast<const u32x4*>(tp)[1];
+      const uint32_t words[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[8 * j + i] = (int8_t)(words[2 * j + (i >> 2)] >> (8 * (i & 3)));
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        // The empty asm keeps the fp32 product and the conversion apart: the
+        // backend would otherwise fold them into one mixed-precision fused
+        // multiply-add with a +0 addend, which turns -0 (s = 0, q < 0) into +0.
+        float v = s * (float)q[8 * j + i];
+        asm volatile("" : "+v"(v));
+        blk[(32 * j + 8 * lq + i) * kDqStride + cbl * 16 + l16] = OH ? f32_to_f16_bits(v) : f32_to_bf16_bits(v);
+      }
+  }
+  __syncthreads();
+  // 128 rows x 16 pieces of 8 columns; pieces past N are skipped.
+  const int n0 = cb0 * kTileCols;
+#pragma unroll
+  for (int m = 0; m < (kGroup * kDqCols / 8) / 256; ++m) {
+    const int c = m * 256 + threadIdx.x;
+    const int row = c >> 4;
+    const int piece = c & 15;
+    const int n = n0 + piece * 8;
+    if (n < N) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(&blk[row * kDqStride + piece * 8]);
+      *reinterpret_cast<u32x4*>(out + (int64_t)(g * kGroup + row) * N + n) = v;
+    }
+  }
+}
+
 dim3 tile_grid(int64_t K, int64_t N) {
   const int64_t lanes = (K / kGroup) * (N / kTileCols) * 64;
   return dim3((unsigned)((lanes + 255) / 256));
@@ -220,6 +298,21 @@ hipError_t launch_unpack(int bits, const void* packed, int64_t K, int64_t N, int
   const dim3 grid = tile_grid(K, N);
   if (bits == 4) unpack_kernel<4><<<grid, 256, 0, st>>>(packed, codes, (int)K, (int)N);
   else           unpack_kernel<8><<<grid, 256, 0, st>>>(packed, codes, (int)K, (int)N);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant(int bits, const void* packed, const void* scales, bool s_bf16, void* out,
+                          bool out_f16, int64_t K, int64_t N, hipStream_t st) {
+  const dim3 grid((unsigned)((N / kTileCols + 7) / 8), (unsigned)(K / kGroup));
+  const auto* sp = static_cast<const uint16_t*>(scales);
+  auto* op = static_cast<uint16_t*>(out);
+  const int k = (int)K, n = (int)N;
+#define QG_D(B, S, H)                                                         \
+  if (bits == B && s_bf16 == S && out_f16 == H)                               \
+    dequant_kernel<B, S, H><<<grid, 256, 0, st>>>(packed, sp, op, k, n);
+  QG_D(4, false, false) QG_D(4, false, true) QG_D(4, true, false) QG_D(4, true, true)
+  QG_D(8, false, false) QG_D(8, false, true) QG_D(8, true, false) QG_D(8, true, true)
+#undef QG_D
   return hipGetLastError();
 }
 

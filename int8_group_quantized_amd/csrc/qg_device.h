@@ -97,4 +97,59 @@ __device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, 
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
+
+// Activation precision of the GEMM kernels: operands travel as raw 32-bit
+// words (two 16-bit values each) and these traits give the matching matrix
+// instruction, the INT4 expansion constant (the smallest value of the format
+// whose unit in the last place is 1: bf16 128, fp16 1024, so OR-ing a nibble
+// u into its mantissa gives magic + u exactly), the offset magic + 8 that the
+// expanded codes carry, the exact pair conversion of INT8 codes, and the RNE
+// output conversion.
+template <bool XH>
+struct Act;
+
+template <>
+struct Act<false> {   // bf16 activations and output
+  static constexpr uint32_t kMagic = 0x43004300u;    // two bf16 128.0
+  static constexpr uint32_t kOffset = 0x43084308u;   // two bf16 136.0
+  static __device__ __forceinline__ f32x4 mma(const u32x4& a, const u32x4& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack2(float a, float b) { return pack_bf16x2(a, b); }
+  static __device__ __forceinline__ uint16_t out(float f) { return f32_to_bf16_bits(f); }
+};
+
+template <>
+struct Act<true> {    // fp16 activations and output
+  static constexpr uint32_t kMagic = 0x64006400u;    // two fp16 1024.0
+  static constexpr uint32_t kOffset = 0x64086408u;   // two fp16 1032.0
+  static __device__ __forceinline__ f32x4 mma(const u32x4& a, const u32x4& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  // Round-toward-zero pair conversion: exact for the integer codes.
+  static __device__ __forceinline__ uint32_t pack2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+  }
+  static __device__ __forceinline__ uint16_t out(float f) { return f32_to_f16_bits(f); }
+};
+
+// Two words of INT8 codes -> eight exact 16-bit integers in the format of A.
+template <class A>
+__device__ __forceinline__ u32x4 int8_words_to_act(uint32_t lo, uint32_t hi) {
+  return u32x4{A::pack2(sbyte_to_f32(lo, 0), sbyte_to_f32(lo, 1)),
+               A::pack2(sbyte_to_f32(lo, 2), sbyte_to_f32(lo, 3)),
+               A::pack2(sbyte_to_f32(hi, 0), sbyte_to_f32(hi, 1)),
+               A::pack2(sbyte_to_f32(hi, 2), sbyte_to_f32(hi, 3))};
+}
+
+// One word of INT4 codes -> eight values magic + u (element order), with the
+// magic held in a vector register by the caller (see the GEMM kernels).
+__device__ __forceinline__ u32x4 int4_word_to_act(uint32_t w, uint32_t magic) {
+  return u32x4{(w & 0x000F000Fu) | magic, ((w >> 4) & 0x000F000Fu) | magic,
+               ((w >> 8) & 0x000F000Fu) | magic, ((w >> 12) & 0x000F000Fu) | magic};
+}
+
 }  // namespace qg

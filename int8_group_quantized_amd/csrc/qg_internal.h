@@ -38,7 +38,7 @@ struct PrefillPlan {
 bool make_prefill_plan(int64_t M, int64_t K, int64_t N, PrefillPlan* plan);
 // Workspace bytes of the prefill path (INT4: counters area + negated offsets).
 size_t prefill_workspace(int bits, const PrefillPlan& p, int64_t K);
-hipError_t launch_gemm_prefill(int bits, const PrefillPlan& p, const void* x,
+hipError_t launch_gemm_prefill(int bits, const PrefillPlan& p, const void* x, bool x_f16,
                                const void* packed, const void* scales, bool s_bf16,
                                void* out, int64_t M, int64_t K, int64_t N, void* ws,
                                hipStream_t st);
@@ -57,7 +57,9 @@ hipError_t launch_prepack(int bits, const int8_t* codes, int64_t K, int64_t N,
                           void* packed, hipStream_t st);
 hipError_t launch_unpack(int bits, const void* packed, int64_t K, int64_t N,
                          int8_t* codes, hipStream_t st);
-hipError_t launch_gemm_small(int bits, const SmallPlan& p, const void* x,
+hipError_t launch_dequant(int bits, const void* packed, const void* scales, bool s_bf16,
+                          void* out, bool out_f16, int64_t K, int64_t N, hipStream_t st);
+hipError_t launch_gemm_small(int bits, const SmallPlan& p, const void* x, bool x_f16,
                              const void* packed, const void* scales, bool s_bf16,
                              void* out, int64_t M, int64_t K, int64_t N,
                              void* workspace, hipStream_t st);

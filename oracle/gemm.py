@@ -29,17 +29,18 @@ from . import numerics
 from .quant import dequant
 
 
-def gemm_ref(x_bits, codes, scale_bits, scale_dtype):
-    """x_bits: bf16 patterns [M, K]; codes int8 [K, N]; scale_bits [K/128, N].
+def gemm_ref(x_bits, codes, scale_bits, scale_dtype, x_dtype="bf16"):
+    """x_bits: 16-bit activation patterns [M, K] (bf16, or fp16 with
+    x_dtype="f16"); codes int8 [K, N]; scale_bits [K/128, N].
 
     Returns the float64 product [M, N].
     """
-    x = numerics.bf16_to_f64(x_bits)
+    x = numerics.act_to_f64(x_bits, x_dtype)
     w = dequant(codes, numerics.scale_bits_to_f64(scale_bits, scale_dtype))
     return x @ w
 
 
-def gemm_ref_at(x_bits, codes, scale_bits, scale_dtype, rows, cols):
+def gemm_ref_at(x_bits, codes, scale_bits, scale_dtype, rows, cols, x_dtype="bf16"):
     """The same definition evaluated only at output positions (rows[i], cols[i]).
 
     For full-size shapes, where the whole product is too slow on a CPU, each
@@ -47,7 +48,7 @@ def gemm_ref_at(x_bits, codes, scale_bits, scale_dtype, rows, cols):
     """
     rows = np.asarray(rows)
     cols = np.asarray(cols)
-    x = numerics.bf16_to_f64(np.asarray(x_bits)[rows])                 # [P, K]
+    x = numerics.act_to_f64(np.asarray(x_bits)[rows], x_dtype)        # [P, K]
     sv = numerics.scale_bits_to_f64(np.asarray(scale_bits)[:, cols], scale_dtype)
     w = dequant(np.asarray(codes)[:, cols], sv)                         # [K, P]
     return np.einsum("pk,kp->p", x, w)

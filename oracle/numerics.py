@@ -63,18 +63,45 @@ def f32_to_f16(x):
         return np.asarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
 
 
-def f64_exact_to_bf16(x):
-    """bf16 RNE of float64 values that are exactly representable in fp32.
-
-    Used only where a result is known to be fp32-exact (the identity-probe
-    products s*q); refuses anything else rather than double-rounding.
-    """
+def _exact_f32(x):
+    """float64 -> fp32 for values that fp32 holds exactly; magnitudes of 2^128
+    and beyond (past the fp32 range, so also past every 16-bit format's
+    overflow threshold) become infinities of the same sign. Anything else
+    that fp32 cannot hold is refused rather than rounded twice."""
     x = np.asarray(x, dtype=np.float64)
-    x32 = x.astype(np.float32)
-    finite = np.isfinite(x)
-    if not np.array_equal(x32.astype(np.float64)[finite], x[finite]):
+    big = np.abs(x) >= 2.0 ** 128
+    with np.errstate(over="ignore"):
+        x32 = np.where(big, np.copysign(np.inf, x), x).astype(np.float32)
+    check = np.isfinite(x) & ~big
+    if not np.array_equal(x32.astype(np.float64)[check], x[check]):
         raise ValueError("value not exactly representable in fp32")
-    return f32_to_bf16(x32)
+    return x32
+
+
+def f64_exact_to_bf16(x):
+    """bf16 RNE of float64 values that are exactly representable in fp32
+    (beyond the fp32 range: infinity).
+
+    Used only where a result is known to be fp32-exact (the products s*q of
+    the identity probe and of dequantization); refuses anything else rather
+    than double-rounding.
+    """
+    return f32_to_bf16(_exact_f32(x))
+
+
+def f64_exact_to_f16(x):
+    """IEEE binary16 RNE of float64 values that are exactly representable in
+    fp32 (same contract as f64_exact_to_bf16); overflow gives infinity."""
+    return f32_to_f16(_exact_f32(x))
+
+
+def act_to_f64(bits, dtype):
+    """Decode 16-bit activations; ``dtype`` is "bf16" or "f16"."""
+    if dtype == "bf16":
+        return bf16_to_f64(bits)
+    if dtype == "f16":
+        return f16_to_f64(bits)
+    raise ValueError(dtype)
 
 
 def scale_bits_to_f64(bits, dtype):

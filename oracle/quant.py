@@ -105,3 +105,20 @@ def dequant(codes, scale_values):
     """
     c = np.asarray(codes).astype(np.float64)
     return c * expand_groups(np.asarray(scale_values, dtype=np.float64), c.shape[0])
+
+
+def dequant_bits(codes, scale_bits, scale_dtype, out_dtype):
+    """The dense dequantized weight s (.) W_q stored in a 16-bit format: the
+    exact product (see dequant) rounded once, to nearest even, into bf16 or
+    fp16 ("bf16" / "f16"); returns uint16 bit patterns [K, N].
+
+    QAD paragraph of arXiv 2607.04244: the student starts from the
+    dequantized weights s (.) W_q; the adaptfm-quant-dflash README (Stage 2)
+    keeps a dense dequantized bf16 twin of the INT4 model.
+    """
+    w = dequant(codes, numerics.scale_bits_to_f64(scale_bits, scale_dtype))
+    if out_dtype == "bf16":
+        return numerics.f64_exact_to_bf16(w)
+    if out_dtype == "f16":
+        return numerics.f64_exact_to_f16(w)
+    raise ValueError(out_dtype)

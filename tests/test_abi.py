@@ -117,3 +117,34 @@ def test_pack_entry_points_validate():
         assert fn(FAKE, 96, 16, FAKE, None) == SHAPE
         assert fn(0, 128, 16, FAKE, None) == NULL
         assert fn(FAKE, 128, 16, MIS, None) == ALIGN
+
+
+def test_f16_gemm_entry_points_validate():
+    L = q.lib()
+    for f in (L.qgemm_w4f16, L.qgemm_w8f16):
+        assert f(FAKE, FAKE, FAKE, 1, FAKE, 1, 100, 512, 0, 0, None) == SHAPE
+        assert f(0, FAKE, FAKE, 1, FAKE, 1, 256, 512, 0, 0, None) == NULL
+        assert f(FAKE, FAKE, FAKE, 2, FAKE, 1, 256, 512, 0, 0, None) == DTYPE
+        assert f(FAKE, FAKE, FAKE, 1, MIS, 1, 256, 512, 0, 0, None) == ALIGN
+        assert f(0, FAKE, FAKE, 1, 0, 0, 256, 512, 0, 0, None) == OK      # M = 0
+    f = L.qgemm_w4f16_plan
+    need = L.qg_workspace_bytes_plan(4, 1, 1024, 64, 1, 1, 4)
+    assert f(FAKE, FAKE, FAKE, 1, FAKE, 1, 1024, 64, FAKE, need - 1, 1, 1, 4, None) == WS
+    assert L.qgemm_w8f16_plan(FAKE, FAKE, FAKE, 0, FAKE, 1, 1024, 64, 0, 0, 3, 1, 1, None) == PLAN
+    # an INT4 prefill call needs the offset workspace
+    need = L.qg_workspace_bytes(4, 100, 256, 64)
+    assert need == 65536 + 128 * 2 * 4
+    assert L.qgemm_w4f16(FAKE, FAKE, FAKE, 1, FAKE, 100, 256, 64, 0, 0, None) == WS
+    assert L.qg_workspace_bytes(8, 100, 256, 64) == 0
+
+
+def test_dequant_entry_points_validate():
+    L = q.lib()
+    for f in (L.qg_dequant_w4, L.qg_dequant_w8):
+        assert f(FAKE, FAKE, 1, 100, 16, FAKE, 0, None) == SHAPE
+        assert f(FAKE, FAKE, 1, 128, 8, FAKE, 0, None) == SHAPE
+        assert f(FAKE, FAKE, 2, 128, 16, FAKE, 0, None) == DTYPE       # fp32 scales
+        assert f(FAKE, FAKE, 1, 128, 16, FAKE, 2, None) == DTYPE       # fp32 output
+        assert f(0, FAKE, 1, 128, 16, FAKE, 0, None) == NULL
+        assert f(FAKE, FAKE, 1, 128, 16, 0, 1, None) == NULL
+        assert f(FAKE, MIS, 1, 128, 16, FAKE, 1, None) == ALIGN

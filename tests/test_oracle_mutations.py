@@ -10,6 +10,7 @@ import numpy as np
 import pytest
 
 from oracle import gemm, layout, numerics, quant
+import test_oracle_dequant as td
 import test_oracle_gemm as tg
 import test_oracle_layout as tl
 import test_oracle_numerics as tn
@@ -131,3 +132,27 @@ def test_bf16_truncation_caught(monkeypatch):
         return (x.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
     monkeypatch.setattr(numerics, "f32_to_bf16", f32_to_bf16)
     _expect_failure(tn.test_bf16_ties_by_hand)
+
+
+def test_f16_rounding_toward_zero_caught(monkeypatch):
+    def f32_to_f16(x):
+        x = np.asarray(x, dtype=np.float32)
+        with np.errstate(over="ignore"):
+            h = x.astype(np.float16)
+        over = np.abs(h.astype(np.float32)) > np.abs(x)
+        return np.where(over, np.nextafter(h, np.float16(0)), h).astype(np.float16).view(np.uint16)
+    monkeypatch.setattr(numerics, "f32_to_f16", f32_to_f16)
+    _expect_failure(td.test_golden_cases)
+
+
+def test_f16_activations_decoded_as_bf16_caught(monkeypatch):
+    monkeypatch.setattr(numerics, "act_to_f64", lambda bits, dtype: numerics.bf16_to_f64(bits))
+    _expect_failure(td.test_f16_one_hot_rows)
+
+
+def test_dequant_truncated_to_bf16_caught(monkeypatch):
+    def f64_exact_to_bf16(x):
+        x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
+        return (x32.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    monkeypatch.setattr(numerics, "f64_exact_to_bf16", f64_exact_to_bf16)
+    _expect_failure(td.test_golden_cases)

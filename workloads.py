@@ -61,11 +61,19 @@ def to_bf16_bits(a):
     return t.view(torch.int16).numpy().view(np.uint16).copy()
 
 
-def activations(M, K, seed, std=1.0):
-    """x ~ N(0, std) rounded to bf16; returns uint16 bit patterns [M, K]."""
+def to_f16_bits(a):
+    """float32 array -> fp16 bit patterns (uint16) via torch's cast."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.float16)
+    return t.view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def activations(M, K, seed, std=1.0, dtype="bf16"):
+    """x ~ N(0, std) rounded to bf16 (or fp16 with dtype="f16"); returns
+    uint16 bit patterns [M, K]."""
     rng = np.random.default_rng(seed)
     x = rng.standard_normal((M, K), dtype=np.float32) * np.float32(std)
-    return to_bf16_bits(x)
+    return to_bf16_bits(x) if dtype == "bf16" else to_f16_bits(x)
 
 
 def codes(K, N, bits, seed, lo=None, hi=None):
