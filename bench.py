@@ -261,6 +261,26 @@ def measure_dequant(torch, q):
             "gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
 
 
+def measure_fake_quant(torch, q):
+    """The fixed-grid fake quantizer on the gate/up weight: fp32 W and fp16
+    scales in, s (.) Q_s(W) out in bf16."""
+    import workloads
+    K, N = 2560, 19456
+    W = torch.from_numpy(workloads.weights(K, N, workloads.seed_for(2, 0, 0))).cuda()
+    s = q.rtn_scales(W, 4)
+    out = torch.empty((K, N), dtype=torch.bfloat16, device="cuda")
+    g = capture(torch, lambda i: q.fake_quant(W, s, 4, out=out), 20)
+    g.replay()
+    ms = time_graphs(torch, [g], reps=5) / 100
+    nbytes = K * N * 4 + (K // 128) * N * 2 + K * N * 2
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    del g, W, out
+    torch.cuda.empty_cache()
+    return {"workload": "fake_quant_w4 fp32 W -> bf16", "K": K, "N": N,
+            "us_per_call": round(ms * 1e3, 2), "gbs": round(gbs, 1),
+            "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def cpu_baseline(seconds):
     """The oracle's product for the headline step, timed on the host."""
     from oracle import gemm, numerics, quant
@@ -344,6 +364,7 @@ def main():
         extra.append(measure_workload(torch, q, 2, act="f16"))
         extra.append(measure_pack(torch, q))
         extra.append(measure_dequant(torch, q))
+        extra.append(measure_fake_quant(torch, q))
 
     if args.copy_calibration:
         copy_calibration(torch)

@@ -213,6 +213,24 @@ qg_status qg_dequant_w8(const void* packed_w, const void* scales, qg_dtype s_dt,
                         int64_t K, int64_t N, void* out, qg_dtype out_dt,
                         void* stream);
 
+/* Fixed-grid fake quantizer of QAD's forward pass (QAD paper, QAD method
+ * paragraph: the student's weights W pass through Q_s under the frozen
+ * scales, trained with a straight-through estimator).
+ *   W      [K,N], w_dt = QG_F32 or QG_BF16
+ *   scales [K/128,N], s_dt = QG_F16 or QG_BF16
+ *   out    [K,N], out_dt = QG_BF16, QG_F16 or QG_F32
+ * out = s * clamp(rne(W / s), lo, hi): the codes of qg_pack_to_grid_w4/w8
+ * (same division, rounding and special cases), the product exact in fp32,
+ * one rounding to nearest even into out_dt. The straight-through estimator
+ * passes the gradient through Q_s unchanged, so the backward pass is the
+ * identity on the incoming gradient and has no entry point of its own. */
+qg_status qg_fake_quant_w4(const void* W, qg_dtype w_dt, const void* scales,
+                           qg_dtype s_dt, int64_t K, int64_t N, void* out,
+                           qg_dtype out_dt, void* stream);
+qg_status qg_fake_quant_w8(const void* W, qg_dtype w_dt, const void* scales,
+                           qg_dtype s_dt, int64_t K, int64_t N, void* out,
+                           qg_dtype out_dt, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -52,6 +52,8 @@ _SIGNATURES = {
                          _INT),
     "qgemm_w8f16_plan": ([_P, _P, _P, _INT, _P, _I64, _I64, _I64, _P, _SZ, _INT, _INT, _INT, _P],
                          _INT),
+    "qg_fake_quant_w4": ([_P, _INT, _P, _INT, _I64, _I64, _P, _INT, _P], _INT),
+    "qg_fake_quant_w8": ([_P, _INT, _P, _INT, _I64, _I64, _P, _INT, _P], _INT),
     "qg_dequant_w4": ([_P, _P, _INT, _I64, _I64, _P, _INT, _P], _INT),
     "qg_dequant_w8": ([_P, _P, _INT, _I64, _I64, _P, _INT, _P], _INT),
 }
@@ -238,3 +240,29 @@ def dequant(packed_w, scales, bits, K, N, dtype=torch.bfloat16, out=None):
     _check(fn, getattr(lib(), fn)(_ptr(packed_w), _ptr(scales), _dt(scales), K, N, _ptr(out),
                                   _dt(out), _stream(packed_w)))
     return out
+
+
+def fake_quant(W, scales, bits, dtype=None, out=None):
+    """s (.) Q_s(W) rounded once to dtype (bf16, fp16 or fp32; default W's)."""
+    _need_cuda(W, scales, out)
+    K, N = W.shape
+    if out is None:
+        out = torch.empty((K, N), dtype=dtype or W.dtype, device=W.device)
+    fn = "qg_fake_quant_w%d" % bits
+    _check(fn, getattr(lib(), fn)(_ptr(W), _dt(W), _ptr(scales), _dt(scales), K, N, _ptr(out),
+                                  _dt(out), _stream(W)))
+    return out
+
+
+class FakeQuantSTE(torch.autograd.Function):
+    """Forward: the fixed-grid fake quantizer on the GPU. Backward: the
+    straight-through estimator, i.e. the incoming gradient unchanged (with
+    respect to W; the frozen scales get none)."""
+
+    @staticmethod
+    def forward(ctx, W, scales, bits):
+        return fake_quant(W, scales, bits)
+
+    @staticmethod
+    def backward(ctx, grad):
+        return grad, None, None

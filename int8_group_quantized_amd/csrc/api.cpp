@@ -120,6 +120,19 @@ qg_status dequant(int bits, const void* packed, const void* scales, qg_dtype s_d
                                      K, N, as_stream(stream)));
 }
 
+qg_status fake_quant(int bits, const void* W, qg_dtype w_dt, const void* scales, qg_dtype s_dt,
+                     int64_t K, int64_t N, void* out, qg_dtype out_dt, void* stream) {
+  qg_status s = check_kn(K, N);
+  if (s != QG_OK) return s;
+  if (w_dt != QG_F32 && w_dt != QG_BF16) return QG_ERR_DTYPE;
+  if (s_dt != QG_F16 && s_dt != QG_BF16) return QG_ERR_DTYPE;
+  if (out_dt != QG_BF16 && out_dt != QG_F16 && out_dt != QG_F32) return QG_ERR_DTYPE;
+  if ((s = check_ptrs({W, scales, out})) != QG_OK) return s;
+  const int kind = out_dt == QG_BF16 ? 0 : (out_dt == QG_F16 ? 1 : 2);
+  return from_hip(qg::launch_fake_quant(bits, W, w_dt == QG_BF16, scales, s_dt == QG_BF16, out,
+                                        kind, K, N, as_stream(stream)));
+}
+
 size_t workspace_bytes(int bits, int64_t M, int64_t K, int64_t N, int nbw, int wk, int splits) {
   if ((bits != 4 && bits != 8) || check_mkn(M, K, N) != QG_OK || M == 0) return 0;
   if (M > kSmallMaxM && nbw == 0 && wk == 0 && splits == 0) {   // prefill kernel
@@ -275,6 +288,16 @@ qg_status qg_dequant_w4(const void* packed_w, const void* scales, qg_dtype s_dt,
 qg_status qg_dequant_w8(const void* packed_w, const void* scales, qg_dtype s_dt, int64_t K,
                         int64_t N, void* out, qg_dtype out_dt, void* stream) {
   return dequant(8, packed_w, scales, s_dt, K, N, out, out_dt, stream);
+}
+
+qg_status qg_fake_quant_w4(const void* W, qg_dtype w_dt, const void* scales, qg_dtype s_dt,
+                           int64_t K, int64_t N, void* out, qg_dtype out_dt, void* stream) {
+  return fake_quant(4, W, w_dt, scales, s_dt, K, N, out, out_dt, stream);
+}
+
+qg_status qg_fake_quant_w8(const void* W, qg_dtype w_dt, const void* scales, qg_dtype s_dt,
+                           int64_t K, int64_t N, void* out, qg_dtype out_dt, void* stream) {
+  return fake_quant(8, W, w_dt, scales, s_dt, K, N, out, out_dt, stream);
 }
 
 }  // extern "C"

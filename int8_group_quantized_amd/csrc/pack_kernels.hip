@@ -5,6 +5,8 @@
 //                  (arXiv 2607.04244, QAD paragraph: updated bf16 weights
 //                  rounded back onto the frozen grid)
 //   prepack/unpack reorder logical codes into / out of the packed tiles
+//   fake_quant     the fixed-grid fake quantizer s (.) Q_s(W) of QAD's
+//                  forward pass, one rounding into bf16, fp16 or fp32
 //   dequant        the dense weight s (.) W_q in bf16 or fp16
 //                  (arXiv 2607.04244, QAD paragraph: the student starts from
 //                  the dequantized weights; README "Stage 2": the dense
@@ -247,6 +249,60 @@ __global__ __launch_bounds__(256) void dequant_kernel(const void* __restrict__ p
   }
 }
 
+// Fake quantization: out[k, n] = s[g, n] * Q_s(W[k, n]) with the codes of
+// pack_to_grid (IEEE division, ties to even, clamp), the product exact in
+// fp32 and one rounding into OUT (0 bf16, 1 fp16, 2 fp32). A thread takes 8
+// consecutive weights of one row (N is a multiple of 16) and their 8 scales.
+template <int BITS, bool W_BF16, bool S_BF16, int OUT>
+__global__ __launch_bounds__(256) void fake_quant_kernel(const void* __restrict__ W,
+                                                         const uint16_t* __restrict__ scales,
+                                                         void* __restrict__ out, int K, int N) {
+  const int64_t e0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  if (e0 >= (int64_t)K * N) return;
+  const int64_t k = e0 / N;
+  const int n = (int)(e0 - k * N);
+  const int g = (int)(k / kGroup);
+  constexpr float lo = (BITS == 4) ? -8.0f : -127.0f;
+  constexpr float hi = (BITS == 4) ? 7.0f : 127.0f;
+  float w[8];
+  if constexpr (W_BF16) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(W) + e0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      w[2 * i] = bf16_bits_to_f32(v[i] & 0xFFFFu);
+      w[2 * i + 1] = bf16_bits_to_f32(v[i] >> 16);
+    }
+  } else {
+    const float* src = static_cast<const float*>(W) + e0;
+    const f32x4 a = *reinterpret_cast<const f32x4*>(src), b = *reinterpret_cast<const f32x4*>(src + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { w[i] = a[i]; w[4 + i] = b[i]; }
+  }
+  const u32x4 sv = *reinterpret_cast<const u32x4*>(scales + (int64_t)g * N + n);
+  float r[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t sb = (i & 1) ? (sv[i >> 1] >> 16) : (sv[i >> 1] & 0xFFFFu);
+    const float s = S_BF16 ? bf16_bits_to_f32(sb) : f16_bits_to_f32(sb);
+    r[i] = s * (float)quantize_to_grid(w[i], s, lo, hi);
+    asm volatile("" : "+v"(r[i]));   // keep the product and the rounding apart
+  }
+  if constexpr (OUT == 2) {
+    float* dst = static_cast<float*>(out) + e0;
+    *reinterpret_cast<f32x4*>(dst) = f32x4{r[0], r[1], r[2], r[3]};
+    *reinterpret_cast<f32x4*>(dst + 4) = f32x4{r[4], r[5], r[6], r[7]};
+  } else {
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t a = OUT == 1 ? f32_to_f16_bits(r[2 * i]) : f32_to_bf16_bits(r[2 * i]);
+      const uint32_t b = OUT == 1 ? f32_to_f16_bits(r[2 * i + 1]) : f32_to_bf16_bits(r[2 * i + 1]);
+      o[i] = a | (b << 16);
+    }
+    *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + e0) = o;
+  }
+}
+
 dim3 tile_grid(int64_t K, int64_t N) {
   const int64_t lanes = (K / kGroup) * (N / kTileCols) * 64;
   return dim3((unsigned)((lanes + 255) / 256));
@@ -313,6 +369,23 @@ hipError_t launch_dequant(int bits, const void* packed, const void* scales, bool
   QG_D(4, false, false) QG_D(4, false, true) QG_D(4, true, false) QG_D(4, true, true)
   QG_D(8, false, false) QG_D(8, false, true) QG_D(8, true, false) QG_D(8, true, true)
 #undef QG_D
+  return hipGetLastError();
+}
+
+hipError_t launch_fake_quant(int bits, const void* W, bool w_bf16, const void* scales, bool s_bf16,
+                             void* out, int out_kind, int64_t K, int64_t N, hipStream_t st) {
+  const int64_t threads = K * N / 8;
+  const dim3 grid((unsigned)((threads + 255) / 256));
+  const auto* sp = static_cast<const uint16_t*>(scales);
+  const int k = (int)K, n = (int)N;
+#define QG_F(B, WB, SB, O)                                                        \
+  if (bits == B && w_bf16 == WB && s_bf16 == SB && out_kind == O)                 \
+    fake_quant_kernel<B, WB, SB, O><<<grid, 256, 0, st>>>(W, sp, out, k, n);
+#define QG_F3(B, WB, SB) QG_F(B, WB, SB, 0) QG_F(B, WB, SB, 1) QG_F(B, WB, SB, 2)
+  QG_F3(4, false, false) QG_F3(4, false, true) QG_F3(4, true, false) QG_F3(4, true, true)
+  QG_F3(8, false, false) QG_F3(8, false, true) QG_F3(8, true, false) QG_F3(8, true, true)
+#undef QG_F3
+#undef QG_F
   return hipGetLastError();
 }
 

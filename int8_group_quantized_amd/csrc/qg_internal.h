@@ -57,6 +57,10 @@ hipError_t launch_prepack(int bits, const int8_t* codes, int64_t K, int64_t N,
                           void* packed, hipStream_t st);
 hipError_t launch_unpack(int bits, const void* packed, int64_t K, int64_t N,
                          int8_t* codes, hipStream_t st);
+// out_kind: 0 bf16, 1 fp16, 2 fp32.
+hipError_t launch_fake_quant(int bits, const void* W, bool w_bf16, const void* scales,
+                             bool s_bf16, void* out, int out_kind, int64_t K, int64_t N,
+                             hipStream_t st);
 hipError_t launch_dequant(int bits, const void* packed, const void* scales, bool s_bf16,
                           void* out, bool out_f16, int64_t K, int64_t N, hipStream_t st);
 hipError_t launch_gemm_small(int bits, const SmallPlan& p, const void* x, bool x_f16,

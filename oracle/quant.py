@@ -122,3 +122,27 @@ def dequant_bits(codes, scale_bits, scale_dtype, out_dtype):
     if out_dtype == "f16":
         return numerics.f64_exact_to_f16(w)
     raise ValueError(out_dtype)
+
+
+def fake_quant(W, scale_bits, scale_dtype, bits, out_dtype):
+    """The fixed-grid fake quantizer of QAD, s (.) Q_s(W), as stored values.
+
+    QAD paragraph of arXiv 2607.04244: the student's weights W pass through
+    Q_s under the frozen scales in the forward pass; the codes are those of
+    q_s (same division and rounding), the product s * q is exact in fp32, and
+    the one rounding is into out_dtype: "bf16" / "f16" give uint16 bit
+    patterns, "f32" gives float32 values.
+
+    The straight-through estimator of the same paragraph (Bengio et al. 2013)
+    passes the gradient through Q_s unchanged, so its backward is the
+    identity on the incoming gradient and needs no separate definition here.
+    """
+    sv = numerics.scale_bits_to_f64(scale_bits, scale_dtype)
+    w = dequant(q_s(W, sv, bits), sv)
+    if out_dtype == "bf16":
+        return numerics.f64_exact_to_bf16(w)
+    if out_dtype == "f16":
+        return numerics.f64_exact_to_f16(w)
+    if out_dtype == "f32":
+        return w.astype(np.float32)
+    raise ValueError(out_dtype)

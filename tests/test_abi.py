@@ -148,3 +148,14 @@ def test_dequant_entry_points_validate():
         assert f(0, FAKE, 1, 128, 16, FAKE, 0, None) == NULL
         assert f(FAKE, FAKE, 1, 128, 16, 0, 1, None) == NULL
         assert f(FAKE, MIS, 1, 128, 16, FAKE, 1, None) == ALIGN
+
+
+def test_fake_quant_entry_points_validate():
+    L = q.lib()
+    for f in (L.qg_fake_quant_w4, L.qg_fake_quant_w8):
+        assert f(FAKE, 2, FAKE, 1, 100, 16, FAKE, 0, None) == SHAPE
+        assert f(FAKE, 1, FAKE, 1, 128, 16, FAKE, 0, None) == DTYPE      # fp16 W
+        assert f(FAKE, 2, FAKE, 2, 128, 16, FAKE, 0, None) == DTYPE      # fp32 scales
+        assert f(FAKE, 2, FAKE, 1, 128, 16, FAKE, 7, None) == DTYPE      # bad output dtype
+        assert f(0, 2, FAKE, 1, 128, 16, FAKE, 2, None) == NULL
+        assert f(FAKE, 0, FAKE, 0, 128, 16, MIS, 0, None) == ALIGN
