@@ -281,6 +281,47 @@ def measure_fake_quant(torch, q):
             "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
 
 
+def measure_grouped(torch, q, bits):
+    """K+V projections of the 5 drafter layers (hidden 2560 -> 2 x 512 each)
+    for a 16-token block, as one grouped launch and as 5 separate launches,
+    over rotating weight copies."""
+    import workloads
+    M, K, N, L = 16, 2560, 1024, 5
+    sdt = "f16" if bits == 4 else "bf16"
+    per = L * (K * N * bits // 8 + (K // 128) * N * 2)
+    copies = max(1, math.ceil(2 * MALL_BYTES / per))
+    sets = []
+    for c in range(copies):
+        if c == 0:
+            base = []
+            for i in range(L):
+                codes = torch.from_numpy(workloads.codes(K, N, bits, 7000 + i)).cuda()
+                sb = workloads.scales(K // 128, N, sdt, 7100 + i).view(np.int16)
+                sc = torch.from_numpy(sb).view(torch.float16 if sdt == "f16" else torch.bfloat16).cuda()
+                base.append((q.prepack(codes, bits), sc, N))
+            sets.append(base)
+        else:
+            sets.append([(p.clone(), sc.clone(), n) for p, sc, n in base])
+    xb = workloads.activations(M, K, 7200)
+    x = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).cuda()
+    outs = [torch.empty((M, N), dtype=torch.bfloat16, device="cuda") for _ in range(L)]
+    ws = torch.zeros(1 << 22, dtype=torch.uint8, device="cuda")
+    g1 = capture(torch, lambda i: q.qgemm_grouped(x, sets[i % copies], bits, outs=outs, ws=ws), 50)
+    g2 = capture(torch, lambda i: [q.qgemm(x, p, sc, bits, n, out=o, ws=ws)
+                                   for (p, sc, n), o in zip(sets[i % copies], outs)], 50)
+    g1.replay()
+    g2.replay()
+    t1 = time_graphs(torch, [g1], reps=4) / 200
+    t2 = time_graphs(torch, [g2], reps=4) / 200
+    nbytes = per + M * K * 2 + L * M * N * 2
+    gbs = nbytes / (t1 * 1e-3) / 1e9
+    del g1, g2, sets, base
+    torch.cuda.empty_cache()
+    return {"workload": "grouped K+V extraction, 5 drafter layers x (2560 -> 1024), W%dA16 M=16" % bits,
+            "us_per_call": round(t1 * 1e3, 2), "us_five_separate_calls": round(t2 * 1e3, 2),
+            "gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def cpu_baseline(seconds):
     """The oracle's product for the headline step, timed on the host."""
     from oracle import gemm, numerics, quant
@@ -365,6 +406,8 @@ def main():
         extra.append(measure_pack(torch, q))
         extra.append(measure_dequant(torch, q))
         extra.append(measure_fake_quant(torch, q))
+        extra.append(measure_grouped(torch, q, 8))
+        extra.append(measure_grouped(torch, q, 4))
 
     if args.copy_calibration:
         copy_calibration(torch)

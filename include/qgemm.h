@@ -231,6 +231,43 @@ qg_status qg_fake_quant_w8(const void* W, qg_dtype w_dt, const void* scales,
                            qg_dtype s_dt, int64_t K, int64_t N, void* out,
                            qg_dtype out_dt, void* stream);
 
+/* Grouped launch: several GEMMs that share x, M and K, each with its own
+ * packed weight, scales, output and N -- a drafter layer set, or the K/V
+ * projections of all drafter layers that the pages' fused-KV path computes
+ * from one input (Qwen3.5-4B-DFlash-W8A16 model card, "Required vLLM
+ * patches", the fused K+V buffer across the 5 layers) -- in one kernel launch
+ * for M <= 16, which saves the per-launch fixed cost of the small shapes
+ * (for M > 16 the items run as consecutive prefill launches).
+ *   items     HOST array of count descriptors (1 <= count <= 16), read during
+ *             the call only; each N a positive multiple of 16
+ *   x, M, K   shared input (bf16, or fp16 for the *f16 variants)
+ *   workspace qg_workspace_bytes_grouped(...) bytes, same rules as above
+ * Each item's output equals what the single GEMM computes on it, bit for
+ * bit when the single call and the group pick the same tiling plan; the
+ * group's plan is chosen for the summed N. Errors as for qgemm_w4a16, plus
+ * QG_ERR_NULL for items == NULL and QG_ERR_SHAPE for a count out of range. */
+typedef struct {
+  const void* packed_w;   /* qg_packed_bytes(bits, K, N) bytes */
+  const void* scales;     /* [K/128, N] */
+  void* out;              /* [M, N] */
+  int64_t N;
+} qg_group_item;
+
+size_t qg_workspace_bytes_grouped(int bits, int64_t M, int64_t K,
+                                  const qg_group_item* items, int count);
+qg_status qgemm_w4a16_grouped(const void* x, const qg_group_item* items, int count,
+                              qg_dtype s_dt, int64_t M, int64_t K, void* workspace,
+                              size_t workspace_bytes, void* stream);
+qg_status qgemm_w8a16_grouped(const void* x, const qg_group_item* items, int count,
+                              qg_dtype s_dt, int64_t M, int64_t K, void* workspace,
+                              size_t workspace_bytes, void* stream);
+qg_status qgemm_w4f16_grouped(const void* x, const qg_group_item* items, int count,
+                              qg_dtype s_dt, int64_t M, int64_t K, void* workspace,
+                              size_t workspace_bytes, void* stream);
+qg_status qgemm_w8f16_grouped(const void* x, const qg_group_item* items, int count,
+                              qg_dtype s_dt, int64_t M, int64_t K, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -26,6 +26,14 @@ _I64 = ctypes.c_int64
 _INT = ctypes.c_int
 _SZ = ctypes.c_size_t
 
+class GroupItem(ctypes.Structure):
+    """qg_group_item of the C ABI."""
+    _fields_ = [("packed_w", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("out", ctypes.c_void_p), ("N", ctypes.c_int64)]
+
+
+_ITEMS = ctypes.POINTER(GroupItem)
+
 _SIGNATURES = {
     "qg_status_str": ([_INT], ctypes.c_char_p),
     "qg_packed_bytes": ([_INT, _I64, _I64], _SZ),
@@ -55,6 +63,11 @@ _SIGNATURES = {
     "qg_fake_quant_w4": ([_P, _INT, _P, _INT, _I64, _I64, _P, _INT, _P], _INT),
     "qg_fake_quant_w8": ([_P, _INT, _P, _INT, _I64, _I64, _P, _INT, _P], _INT),
     "qg_dequant_w4": ([_P, _P, _INT, _I64, _I64, _P, _INT, _P], _INT),
+    "qg_workspace_bytes_grouped": ([_INT, _I64, _I64, _ITEMS, _INT], _SZ),
+    "qgemm_w4a16_grouped": ([_P, _ITEMS, _INT, _INT, _I64, _I64, _P, _SZ, _P], _INT),
+    "qgemm_w8a16_grouped": ([_P, _ITEMS, _INT, _INT, _I64, _I64, _P, _SZ, _P], _INT),
+    "qgemm_w4f16_grouped": ([_P, _ITEMS, _INT, _INT, _I64, _I64, _P, _SZ, _P], _INT),
+    "qgemm_w8f16_grouped": ([_P, _ITEMS, _INT, _INT, _I64, _I64, _P, _SZ, _P], _INT),
     "qg_dequant_w8": ([_P, _P, _INT, _I64, _I64, _P, _INT, _P], _INT),
 }
 
@@ -266,3 +279,26 @@ class FakeQuantSTE(torch.autograd.Function):
     @staticmethod
     def backward(ctx, grad):
         return grad, None, None
+
+
+def qgemm_grouped(x, weights, bits, outs=None, ws=None):
+    """One launch of several GEMMs sharing x: weights is a list of
+    (packed_w, scales, N); returns the list of outputs [M, N_i]."""
+    _need_cuda(x)
+    if x.dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError("x must be bf16 or fp16")
+    M, K = x.shape
+    if outs is None:
+        outs = [torch.empty((M, n), dtype=x.dtype, device=x.device) for _, _, n in weights]
+    for (p, sc, _), o in zip(weights, outs):
+        _need_cuda(p, sc, o)
+    items = (GroupItem * len(weights))(*[GroupItem(p.data_ptr(), sc.data_ptr(), o.data_ptr(), n)
+                                         for (p, sc, n), o in zip(weights, outs)])
+    need = int(lib().qg_workspace_bytes_grouped(bits, M, K, items, len(weights)))
+    if ws is None and need > 0:
+        ws = workspace(x.device, need)
+    ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
+    fn = "qgemm_w%d%s_grouped" % (bits, "a16" if x.dtype == torch.bfloat16 else "f16")
+    _check(fn, getattr(lib(), fn)(_ptr(x), items, len(weights), _dt(weights[0][1]), M, K,
+                                  _ptr(ws), ws_bytes, _stream(x)))
+    return outs

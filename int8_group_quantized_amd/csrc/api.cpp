@@ -41,6 +41,8 @@ qg_status check_ptrs(std::initializer_list<const void*> ptrs) {
 
 qg_status from_hip(hipError_t e) { return e == hipSuccess ? QG_OK : QG_ERR_HIP; }
 
+bool s_bf16(qg_dtype d) { return d == QG_BF16; }
+
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
 qg_status rtn_scales(int bits, const void* W, qg_dtype w_dt, int64_t K, int64_t N, void* scales,
@@ -95,8 +97,8 @@ qg_status gemm(int bits, bool x_f16, const void* x, const void* packed, const vo
       if (ws == nullptr || ws_bytes < need) return QG_ERR_WORKSPACE;
       if (!aligned16(ws)) return QG_ERR_ALIGN;
     }
-    return from_hip(qg::launch_gemm_prefill(bits, pp, x, x_f16, packed, scales, s_dt == QG_BF16,
-                                            out, M, K, N, ws, as_stream(stream)));
+    return from_hip(qg::launch_gemm_prefill(bits, pp, x, x_f16, packed, scales, s_bf16(s_dt), out,
+                                            M, K, N, ws, as_stream(stream)));
   }
   qg::SmallPlan plan;
   if (!qg::make_small_plan(bits, M, K, N, nbw, wk, splits, &plan)) return QG_ERR_PLAN;
@@ -105,8 +107,94 @@ qg_status gemm(int bits, bool x_f16, const void* x, const void* packed, const vo
     if (ws == nullptr || ws_bytes < need) return QG_ERR_WORKSPACE;
     if (!aligned16(ws)) return QG_ERR_ALIGN;
   }
-  return from_hip(qg::launch_gemm_small(bits, plan, x, x_f16, packed, scales, s_dt == QG_BF16,
-                                        out, M, K, N, ws, as_stream(stream)));
+  qg::GroupArgs g;
+  g.count = 1;
+  g.n[0] = (int)N;
+  g.packed[0] = static_cast<const char*>(packed);
+  g.scales[0] = static_cast<const uint16_t*>(scales);
+  g.out[0] = static_cast<uint16_t*>(out);
+  qg::small_plan_group(plan, &g);
+  return from_hip(qg::launch_gemm_small(bits, plan, x, x_f16, g, s_bf16(s_dt), M, K, ws,
+                                        as_stream(stream)));
+}
+
+// Grouped GEMMs sharing x, M and K: checks every item, then one launch of the
+// small-M kernel over all of them (M <= 16), or one prefill launch per item.
+constexpr int64_t kMaxCounters = 65536 / 4;   // 32-bit arrival counters at the workspace start
+
+qg_status grouped_plan(int bits, int64_t M, int64_t K, const qg_group_item* items, int count,
+                       qg::SmallPlan* plan, qg::GroupArgs* g) {
+  if (items == nullptr) return QG_ERR_NULL;
+  if (count < 1 || count > qg::GroupArgs::kMax) return QG_ERR_SHAPE;
+  int64_t ntot = 0;
+  for (int i = 0; i < count; ++i) {
+    const qg_status s = check_mkn(M, K, items[i].N);
+    if (s != QG_OK) return s;
+    ntot += items[i].N;
+  }
+  qg_status s = check_mkn(M, K, ntot);
+  if (s != QG_OK) return s;
+  if (M > kSmallMaxM) return QG_OK;
+  if (M == 0) return QG_OK;
+  if (!qg::make_small_plan(bits, M, K, ntot, 0, 0, 0, plan)) return QG_ERR_SHAPE;
+  g->count = count;
+  for (int i = 0; i < count; ++i) {
+    g->n[i] = (int)items[i].N;
+    g->packed[i] = static_cast<const char*>(items[i].packed_w);
+    g->scales[i] = static_cast<const uint16_t*>(items[i].scales);
+    g->out[i] = static_cast<uint16_t*>(items[i].out);
+  }
+  qg::small_plan_group(*plan, g);
+  if (plan->splits > 1 && (int64_t)g->wg_prefix[count] * plan->row_blocks > kMaxCounters)
+    return QG_ERR_SHAPE;
+  return QG_OK;
+}
+
+size_t grouped_workspace(int bits, int64_t M, int64_t K, const qg_group_item* items, int count) {
+  if (bits != 4 && bits != 8) return 0;
+  qg::SmallPlan plan;
+  qg::GroupArgs g;
+  if (grouped_plan(bits, M, K, items, count, &plan, &g) != QG_OK || M == 0) return 0;
+  if (M > kSmallMaxM) {
+    qg::PrefillPlan pp;
+    if (!qg::make_prefill_plan(M, K, items[0].N, &pp)) return 0;
+    return qg::prefill_workspace(bits, pp, K);   // depends on M and K only
+  }
+  return qg::small_plan_workspace(plan, M, g.n_total);
+}
+
+qg_status gemm_grouped(int bits, bool x_f16, const void* x, const qg_group_item* items, int count,
+                       qg_dtype s_dt, int64_t M, int64_t K, void* ws, size_t ws_bytes,
+                       void* stream) {
+  if (s_dt != QG_F16 && s_dt != QG_BF16) return QG_ERR_DTYPE;
+  qg::SmallPlan plan;
+  qg::GroupArgs g;
+  qg_status s = grouped_plan(bits, M, K, items, count, &plan, &g);
+  if (s != QG_OK) return s;
+  for (int i = 0; i < count; ++i)
+    if ((s = check_ptrs({items[i].packed_w, items[i].scales})) != QG_OK) return s;
+  if (M == 0) return QG_OK;
+  if ((s = check_ptrs({x})) != QG_OK) return s;
+  for (int i = 0; i < count; ++i)
+    if ((s = check_ptrs({items[i].out})) != QG_OK) return s;
+  const size_t need = grouped_workspace(bits, M, K, items, count);
+  if (need > 0) {
+    if (ws == nullptr || ws_bytes < need) return QG_ERR_WORKSPACE;
+    if (!aligned16(ws)) return QG_ERR_ALIGN;
+  }
+  if (M > kSmallMaxM) {
+    for (int i = 0; i < count; ++i) {
+      qg::PrefillPlan pp;
+      if (!qg::make_prefill_plan(M, K, items[i].N, &pp)) return QG_ERR_SHAPE;
+      s = from_hip(qg::launch_gemm_prefill(bits, pp, x, x_f16, items[i].packed_w, items[i].scales,
+                                           s_bf16(s_dt), items[i].out, M, K, items[i].N, ws,
+                                           as_stream(stream)));
+      if (s != QG_OK) return s;
+    }
+    return QG_OK;
+  }
+  return from_hip(qg::launch_gemm_small(bits, plan, x, x_f16, g, s_bf16(s_dt), M, K, ws,
+                                        as_stream(stream)));
 }
 
 qg_status dequant(int bits, const void* packed, const void* scales, qg_dtype s_dt, int64_t K,
@@ -298,6 +386,35 @@ qg_status qg_fake_quant_w4(const void* W, qg_dtype w_dt, const void* scales, qg_
 qg_status qg_fake_quant_w8(const void* W, qg_dtype w_dt, const void* scales, qg_dtype s_dt,
                            int64_t K, int64_t N, void* out, qg_dtype out_dt, void* stream) {
   return fake_quant(8, W, w_dt, scales, s_dt, K, N, out, out_dt, stream);
+}
+
+size_t qg_workspace_bytes_grouped(int bits, int64_t M, int64_t K, const qg_group_item* items,
+                                  int count) {
+  return grouped_workspace(bits, M, K, items, count);
+}
+
+qg_status qgemm_w4a16_grouped(const void* x, const qg_group_item* items, int count, qg_dtype s_dt,
+                              int64_t M, int64_t K, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  return gemm_grouped(4, false, x, items, count, s_dt, M, K, workspace, workspace_bytes, stream);
+}
+
+qg_status qgemm_w8a16_grouped(const void* x, const qg_group_item* items, int count, qg_dtype s_dt,
+                              int64_t M, int64_t K, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  return gemm_grouped(8, false, x, items, count, s_dt, M, K, workspace, workspace_bytes, stream);
+}
+
+qg_status qgemm_w4f16_grouped(const void* x, const qg_group_item* items, int count, qg_dtype s_dt,
+                              int64_t M, int64_t K, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  return gemm_grouped(4, true, x, items, count, s_dt, M, K, workspace, workspace_bytes, stream);
+}
+
+qg_status qgemm_w8f16_grouped(const void* x, const qg_group_item* items, int count, qg_dtype s_dt,
+                              int64_t M, int64_t K, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  return gemm_grouped(8, true, x, items, count, s_dt, M, K, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -104,10 +104,8 @@ struct Batch {
 
 template <int BITS, bool SBF, bool XH, int MR, int NBW, int WN, int WK>
 __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_small_kernel(
-    const uint16_t* __restrict__ x, const char* packed, const uint16_t* scales,
-    uint16_t* __restrict__ out,
-    uint32_t* __restrict__ counters, float* __restrict__ partials, int M, int K, int N,
-    int splits, int gps, int sg) {
+    const uint16_t* __restrict__ x, const GroupArgs ga, uint32_t* __restrict__ counters,
+    float* __restrict__ partials, int M, int K, int splits, int gps, int sg) {
   constexpr int NT = 64 * WN * WK;
   constexpr int NW = WN * WK;
   constexpr int TB = Tile<BITS>::bytes;
@@ -122,9 +120,18 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_small_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wn = wave % WN;
   const int wk = wave / WN;
+  // The GEMM of the group this workgroup belongs to (a scalar search over at
+  // most 16 prefix entries).
+  int item = 0;
+  for (int i = 1; i < ga.count; ++i)
+    if ((int)blockIdx.x >= ga.wg_prefix[i]) item = i;
+  const int N = ga.n[item];
+  const char* packed = ga.packed[item];
+  const uint16_t* scales = ga.scales[item];
+  uint16_t* out = ga.out[item];
   const int G = K >> 7;
   const int NB = N >> 4;
-  const int cb0 = (blockIdx.x * WN + wn) * NBW;
+  const int cb0 = (((int)blockIdx.x - ga.wg_prefix[item]) * WN + wn) * NBW;
   const int nvalid = min(NBW, NB - cb0);     // column blocks this wave owns (may be <= 0)
   const int split = blockIdx.y;
   const int row0 = blockIdx.z * 16;
@@ -343,7 +350,8 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_small_kernel(
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * lq + e;
           if (r < mrows)
-            store_coherent(&partials[((int64_t)split * M + row0 + r) * N + n], acc[c][e]);
+            store_coherent(&partials[((int64_t)split * M + row0 + r) * ga.n_total + ga.col_prefix[item] + n],
+                           acc[c][e]);
         }
       }
     }
@@ -371,7 +379,8 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_small_kernel(
           if (r < mrows) {
             float sum = 0.0f;
             for (int sp = 0; sp < splits; ++sp)
-              sum += load_coherent(&partials[((int64_t)sp * M + row0 + r) * N + n]);
+              sum += load_coherent(
+                  &partials[((int64_t)sp * M + row0 + r) * ga.n_total + ga.col_prefix[item] + n]);
             out[(int64_t)(row0 + r) * N + n] = A::out(sum);
           }
         }
@@ -383,10 +392,9 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_small_kernel(
 }
 
 template <int BITS, bool SBF, bool XH, int MR, int NBW, int WN, int WK>
-hipError_t launch_variant(const SmallPlan& p, const void* x, const void* packed,
-                          const void* scales, void* out, int64_t M, int64_t K, int64_t N,
-                          void* ws, hipStream_t st) {
-  const dim3 grid((unsigned)p.wgs_n, (unsigned)p.splits, (unsigned)p.row_blocks);
+hipError_t launch_variant(const SmallPlan& p, const void* x, const GroupArgs& g, int64_t M,
+                          int64_t K, void* ws, hipStream_t st) {
+  const dim3 grid((unsigned)g.wg_prefix[g.count], (unsigned)p.splits, (unsigned)p.row_blocks);
   uint32_t* counters = nullptr;
   float* partials = nullptr;
   if (p.splits > 1) {
@@ -395,18 +403,17 @@ hipError_t launch_variant(const SmallPlan& p, const void* x, const void* packed,
   }
   const size_t lds = small_plan_lds_bytes(p, M);
   gemm_small_kernel<BITS, SBF, XH, MR, NBW, WN, WK><<<grid, 64 * WN * WK, lds, st>>>(
-      static_cast<const uint16_t*>(x), static_cast<const char*>(packed),
-      static_cast<const uint16_t*>(scales), static_cast<uint16_t*>(out), counters, partials,
-      (int)M, (int)K, (int)N, p.splits, p.gps, p.sg);
+      static_cast<const uint16_t*>(x), g, counters, partials, (int)M, (int)K, p.splits, p.gps,
+      p.sg);
   return hipGetLastError();
 }
 
 template <int BITS, bool SBF, bool XH, int MR>
-hipError_t launch_shape(const SmallPlan& p, const void* x, const void* packed, const void* scales,
-                        void* out, int64_t M, int64_t K, int64_t N, void* ws, hipStream_t st) {
+hipError_t launch_shape(const SmallPlan& p, const void* x, const GroupArgs& g, int64_t M,
+                        int64_t K, void* ws, hipStream_t st) {
 #define QG_V(NBW, WN, WK)                                                                    \
   if (p.nbw == NBW && p.wn == WN && p.wk == WK)                                              \
-    return launch_variant<BITS, SBF, XH, MR, NBW, WN, WK>(p, x, packed, scales, out, M, K, N, ws, st);
+    return launch_variant<BITS, SBF, XH, MR, NBW, WN, WK>(p, x, g, M, K, ws, st);
   QG_V(1, 4, 1) QG_V(1, 2, 2) QG_V(1, 1, 4) QG_V(1, 1, 8)
   QG_V(2, 4, 1) QG_V(2, 1, 4)
   QG_V(4, 4, 1) QG_V(4, 1, 4)
@@ -505,12 +512,25 @@ size_t small_plan_workspace(const SmallPlan& p, int64_t M, int64_t N) {
   return (size_t)kCounterBytes + (size_t)p.splits * (size_t)M * (size_t)N * sizeof(float);
 }
 
+void small_plan_group(const SmallPlan& p, GroupArgs* g) {
+  const int per = p.wn * p.nbw;                      // column blocks per workgroup
+  int wg = 0, col = 0;
+  for (int i = 0; i < g->count; ++i) {
+    g->wg_prefix[i] = wg;
+    g->col_prefix[i] = col;
+    wg += (g->n[i] / kTileCols + per - 1) / per;
+    col += g->n[i];
+  }
+  g->wg_prefix[g->count] = wg;
+  g->n_total = col;
+}
+
 hipError_t launch_gemm_small(int bits, const SmallPlan& p, const void* x, bool x_f16,
-                             const void* packed, const void* scales, bool s_bf16, void* out,
-                             int64_t M, int64_t K, int64_t N, void* ws, hipStream_t st) {
+                             const GroupArgs& g, bool s_bf16, int64_t M, int64_t K, void* ws,
+                             hipStream_t st) {
 #define QG_B(B, S, H, R)                                                                  \
   if (bits == B && s_bf16 == S && x_f16 == H && p.mr == R)                                \
-    return launch_shape<B, S, H, R>(p, x, packed, scales, out, M, K, N, ws, st);
+    return launch_shape<B, S, H, R>(p, x, g, M, K, ws, st);
   QG_B(4, false, false, 1) QG_B(4, false, false, 16) QG_B(4, true, false, 1) QG_B(4, true, false, 16)
   QG_B(8, false, false, 1) QG_B(8, false, false, 16) QG_B(8, true, false, 1) QG_B(8, true, false, 16)
   QG_B(4, false, true, 1) QG_B(4, false, true, 16) QG_B(4, true, true, 1) QG_B(4, true, true, 16)

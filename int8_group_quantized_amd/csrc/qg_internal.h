@@ -14,6 +14,23 @@ namespace qg {
 // wavefronts of a 4-wave workgroup split the K range of the workgroup;
 // `splits` workgroups split K across the grid (fp32 partials + a last-arrival
 // reduction). Rows are covered 16 at a time (grid z).
+// Several GEMMs that share x, M and K (a layer's Linear set, or the K/V
+// projections of every drafter layer), run by one launch of the small-M
+// kernel: item i owns column workgroups [wg_prefix[i], wg_prefix[i+1]) and
+// columns [col_prefix[i], col_prefix[i] + n[i]) of the concatenated split-K
+// partials. A single GEMM is a group of one.
+struct GroupArgs {
+  static constexpr int kMax = 16;
+  int count = 0;
+  int n_total = 0;
+  int wg_prefix[kMax + 1] = {};
+  int col_prefix[kMax] = {};
+  int n[kMax] = {};
+  const char* packed[kMax] = {};
+  const uint16_t* scales[kMax] = {};
+  uint16_t* out[kMax] = {};
+};
+
 struct SmallPlan {
   int bits = 4;
   int mr = 16;        // 1: single-row layout of x in LDS; 16: rows padded to 16
@@ -63,9 +80,10 @@ hipError_t launch_fake_quant(int bits, const void* W, bool w_bf16, const void* s
                              hipStream_t st);
 hipError_t launch_dequant(int bits, const void* packed, const void* scales, bool s_bf16,
                           void* out, bool out_f16, int64_t K, int64_t N, hipStream_t st);
+// Fills the group's workgroup prefixes for plan p (wgs_n is per item there).
+void small_plan_group(const SmallPlan& p, GroupArgs* g);
 hipError_t launch_gemm_small(int bits, const SmallPlan& p, const void* x, bool x_f16,
-                             const void* packed, const void* scales, bool s_bf16,
-                             void* out, int64_t M, int64_t K, int64_t N,
+                             const GroupArgs& g, bool s_bf16, int64_t M, int64_t K,
                              void* workspace, hipStream_t st);
 
 }  // namespace qg

@@ -159,3 +159,26 @@ def test_fake_quant_entry_points_validate():
         assert f(FAKE, 2, FAKE, 1, 128, 16, FAKE, 7, None) == DTYPE      # bad output dtype
         assert f(0, 2, FAKE, 1, 128, 16, FAKE, 2, None) == NULL
         assert f(FAKE, 0, FAKE, 0, 128, 16, MIS, 0, None) == ALIGN
+
+
+def _items(*ns, p=FAKE):
+    return (b.GroupItem * len(ns))(*[b.GroupItem(p, FAKE, FAKE, n) for n in ns])
+
+
+def test_grouped_entry_points_validate():
+    L = q.lib()
+    for f in (L.qgemm_w4a16_grouped, L.qgemm_w8a16_grouped, L.qgemm_w4f16_grouped,
+              L.qgemm_w8f16_grouped):
+        assert f(FAKE, None, 1, 1, 1, 256, 0, 0, None) == NULL
+        assert f(FAKE, _items(512), 0, 1, 1, 256, 0, 0, None) == SHAPE
+        assert f(FAKE, _items(*([512] * 17)), 17, 1, 1, 256, 0, 0, None) == SHAPE
+        assert f(FAKE, _items(512, 24), 2, 1, 1, 256, 0, 0, None) == SHAPE     # N % 16
+        assert f(FAKE, _items(512), 1, 1, 1, 100, 0, 0, None) == SHAPE       # K % 128
+        assert f(FAKE, _items(512, 512, p=0), 2, 1, 1, 256, 0, 0, None) == NULL
+        assert f(FAKE, _items(512), 1, 2, 1, 256, 0, 0, None) == DTYPE
+        assert f(MIS, _items(512), 1, 1, 1, 256, 0, 0, None) == ALIGN
+        assert f(0, _items(512), 1, 1, 0, 256, 0, 0, None) == OK             # M = 0
+    # a group needs no more workspace than its plan; one item matches the single call
+    assert L.qg_workspace_bytes_grouped(4, 16, 9728, _items(2560), 1) == \
+        L.qg_workspace_bytes(4, 16, 9728, 2560)
+    assert L.qg_workspace_bytes_grouped(4, 16, 9728, None, 1) == 0
