@@ -109,10 +109,10 @@ qg_status gemm(int bits, bool x_f16, const void* x, const void* packed, const vo
   }
   qg::GroupArgs g;
   g.count = 1;
-  g.n[0] = (int)N;
-  g.packed[0] = static_cast<const char*>(packed);
-  g.scales[0] = static_cast<const uint16_t*>(scales);
-  g.out[0] = static_cast<uint16_t*>(out);
+  g.item[0].n = (int)N;
+  g.item[0].packed = static_cast<const char*>(packed);
+  g.item[0].scales = static_cast<const uint16_t*>(scales);
+  g.item[0].out = static_cast<uint16_t*>(out);
   qg::small_plan_group(plan, &g);
   return from_hip(qg::launch_gemm_small(bits, plan, x, x_f16, g, s_bf16(s_dt), M, K, ws,
                                         as_stream(stream)));
@@ -139,13 +139,13 @@ qg_status grouped_plan(int bits, int64_t M, int64_t K, const qg_group_item* item
   if (!qg::make_small_plan(bits, M, K, ntot, 0, 0, 0, plan)) return QG_ERR_SHAPE;
   g->count = count;
   for (int i = 0; i < count; ++i) {
-    g->n[i] = (int)items[i].N;
-    g->packed[i] = static_cast<const char*>(items[i].packed_w);
-    g->scales[i] = static_cast<const uint16_t*>(items[i].scales);
-    g->out[i] = static_cast<uint16_t*>(items[i].out);
+    g->item[i].n = (int)items[i].N;
+    g->item[i].packed = static_cast<const char*>(items[i].packed_w);
+    g->item[i].scales = static_cast<const uint16_t*>(items[i].scales);
+    g->item[i].out = static_cast<uint16_t*>(items[i].out);
   }
   qg::small_plan_group(*plan, g);
-  if (plan->splits > 1 && (int64_t)g->wg_prefix[count] * plan->row_blocks > kMaxCounters)
+  if (plan->splits > 1 && (int64_t)g->wg_total * plan->row_blocks > kMaxCounters)
     return QG_ERR_SHAPE;
   return QG_OK;
 }

@@ -102,10 +102,10 @@ struct Batch {
                                        : (NBW == 1 ? 2 : 1);
 };
 
-template <int BITS, bool SBF, bool XH, int MR, int NBW, int WN, int WK>
+template <int BITS, bool SBF, bool XH, bool GR, int MR, int NBW, int WN, int WK>
 __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_small_kernel(
-    const uint16_t* __restrict__ x, const GroupArgs ga, uint32_t* __restrict__ counters,
-    float* __restrict__ partials, int M, int K, int splits, int gps, int sg) {
+    const uint16_t* __restrict__ x, uint32_t* __restrict__ counters,
+    float* __restrict__ partials, int M, int K, int splits, int gps, int sg, const GroupArgs ga) {
   constexpr int NT = 64 * WN * WK;
   constexpr int NW = WN * WK;
   constexpr int TB = Tile<BITS>::bytes;
@@ -121,17 +121,22 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_small_kernel(
   const int wn = wave % WN;
   const int wk = wave / WN;
   // The GEMM of the group this workgroup belongs to (a scalar search over at
-  // most 16 prefix entries).
+  // most 16 prefix entries); a single GEMM is item 0, read at fixed offsets.
   int item = 0;
-  for (int i = 1; i < ga.count; ++i)
-    if ((int)blockIdx.x >= ga.wg_prefix[i]) item = i;
-  const int N = ga.n[item];
-  const char* packed = ga.packed[item];
-  const uint16_t* scales = ga.scales[item];
-  uint16_t* out = ga.out[item];
+  if constexpr (GR) {
+    for (int i = 1; i < ga.count; ++i)
+      if ((int)blockIdx.x >= ga.item[i].wg_first) item = i;
+  }
+  const GroupItem& it = ga.item[item];
+  const int N = it.n;
+  const int wg0 = GR ? it.wg_first : 0;
+  const int colp = GR ? it.col_first : 0;
+  const char* packed = it.packed;
+  const uint16_t* scales = it.scales;
+  uint16_t* out = it.out;
   const int G = K >> 7;
   const int NB = N >> 4;
-  const int cb0 = (((int)blockIdx.x - ga.wg_prefix[item]) * WN + wn) * NBW;
+  const int cb0 = (((int)blockIdx.x - wg0) * WN + wn) * NBW;
   const int nvalid = min(NBW, NB - cb0);     // column blocks this wave owns (may be <= 0)
   const int split = blockIdx.y;
   const int row0 = blockIdx.z * 16;
@@ -350,7 +355,7 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_small_kernel(
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * lq + e;
           if (r < mrows)
-            store_coherent(&partials[((int64_t)split * M + row0 + r) * ga.n_total + ga.col_prefix[item] + n],
+            store_coherent(&partials[((int64_t)split * M + row0 + r) * ga.n_total + colp + n],
                            acc[c][e]);
         }
       }
@@ -380,7 +385,7 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_small_kernel(
             float sum = 0.0f;
             for (int sp = 0; sp < splits; ++sp)
               sum += load_coherent(
-                  &partials[((int64_t)sp * M + row0 + r) * ga.n_total + ga.col_prefix[item] + n]);
+                  &partials[((int64_t)sp * M + row0 + r) * ga.n_total + colp + n]);
             out[(int64_t)(row0 + r) * N + n] = A::out(sum);
           }
         }
@@ -391,10 +396,10 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_small_kernel(
     __hip_atomic_store(&counters[cidx], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int BITS, bool SBF, bool XH, int MR, int NBW, int WN, int WK>
+template <int BITS, bool SBF, bool XH, bool GR, int MR, int NBW, int WN, int WK>
 hipError_t launch_variant(const SmallPlan& p, const void* x, const GroupArgs& g, int64_t M,
                           int64_t K, void* ws, hipStream_t st) {
-  const dim3 grid((unsigned)g.wg_prefix[g.count], (unsigned)p.splits, (unsigned)p.row_blocks);
+  const dim3 grid((unsigned)g.wg_total, (unsigned)p.splits, (unsigned)p.row_blocks);
   uint32_t* counters = nullptr;
   float* partials = nullptr;
   if (p.splits > 1) {
@@ -402,18 +407,27 @@ hipError_t launch_variant(const SmallPlan& p, const void* x, const GroupArgs& g,
     partials = reinterpret_cast<float*>(static_cast<char*>(ws) + kCounterBytes);
   }
   const size_t lds = small_plan_lds_bytes(p, M);
-  gemm_small_kernel<BITS, SBF, XH, MR, NBW, WN, WK><<<grid, 64 * WN * WK, lds, st>>>(
-      static_cast<const uint16_t*>(x), g, counters, partials, (int)M, (int)K, p.splits, p.gps,
-      p.sg);
+  gemm_small_kernel<BITS, SBF, XH, GR, MR, NBW, WN, WK><<<grid, 64 * WN * WK, lds, st>>>(
+      static_cast<const uint16_t*>(x), counters, partials, (int)M, (int)K, p.splits, p.gps,
+      p.sg, g);
   return hipGetLastError();
 }
 
 template <int BITS, bool SBF, bool XH, int MR>
 hipError_t launch_shape(const SmallPlan& p, const void* x, const GroupArgs& g, int64_t M,
                         int64_t K, void* ws, hipStream_t st) {
+  if (g.count > 1) {
+    // Groups always take the library's own plan, which uses these shapes.
+#define QG_G(NBW, WN, WK)                                                                    \
+    if (p.nbw == NBW && p.wn == WN && p.wk == WK)                                            \
+      return launch_variant<BITS, SBF, XH, true, MR, NBW, WN, WK>(p, x, g, M, K, ws, st);
+    QG_G(1, 1, 4) QG_G(2, 4, 1) QG_G(1, 2, 2)
+#undef QG_G
+    return hipErrorInvalidValue;
+  }
 #define QG_V(NBW, WN, WK)                                                                    \
   if (p.nbw == NBW && p.wn == WN && p.wk == WK)                                              \
-    return launch_variant<BITS, SBF, XH, MR, NBW, WN, WK>(p, x, g, M, K, ws, st);
+    return launch_variant<BITS, SBF, XH, false, MR, NBW, WN, WK>(p, x, g, M, K, ws, st);
   QG_V(1, 4, 1) QG_V(1, 2, 2) QG_V(1, 1, 4) QG_V(1, 1, 8)
   QG_V(2, 4, 1) QG_V(2, 1, 4)
   QG_V(4, 4, 1) QG_V(4, 1, 4)
@@ -516,12 +530,12 @@ void small_plan_group(const SmallPlan& p, GroupArgs* g) {
   const int per = p.wn * p.nbw;                      // column blocks per workgroup
   int wg = 0, col = 0;
   for (int i = 0; i < g->count; ++i) {
-    g->wg_prefix[i] = wg;
-    g->col_prefix[i] = col;
-    wg += (g->n[i] / kTileCols + per - 1) / per;
-    col += g->n[i];
+    g->item[i].wg_first = wg;
+    g->item[i].col_first = col;
+    wg += (g->item[i].n / kTileCols + per - 1) / per;
+    col += g->item[i].n;
   }
-  g->wg_prefix[g->count] = wg;
+  g->wg_total = wg;
   g->n_total = col;
 }
 

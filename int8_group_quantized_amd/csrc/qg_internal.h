@@ -16,19 +16,27 @@ namespace qg {
 // reduction). Rows are covered 16 at a time (grid z).
 // Several GEMMs that share x, M and K (a layer's Linear set, or the K/V
 // projections of every drafter layer), run by one launch of the small-M
-// kernel: item i owns column workgroups [wg_prefix[i], wg_prefix[i+1]) and
-// columns [col_prefix[i], col_prefix[i] + n[i]) of the concatenated split-K
-// partials. A single GEMM is a group of one.
+// kernel: item i owns column workgroups [wg_first, next item's wg_first) and
+// columns [col_first, col_first + n) of the concatenated split-K partials. A
+// single GEMM is a group of one. The items are stored as an array of structs
+// so that a group of one reads only the first 40 bytes of the table.
+struct GroupItem {
+  const char* packed = nullptr;
+  const uint16_t* scales = nullptr;
+  uint16_t* out = nullptr;
+  int n = 0;
+  int wg_first = 0;
+  int col_first = 0;
+  int pad = 0;
+};
+
 struct GroupArgs {
   static constexpr int kMax = 16;
   int count = 0;
   int n_total = 0;
-  int wg_prefix[kMax + 1] = {};
-  int col_prefix[kMax] = {};
-  int n[kMax] = {};
-  const char* packed[kMax] = {};
-  const uint16_t* scales[kMax] = {};
-  uint16_t* out[kMax] = {};
+  int wg_total = 0;
+  int pad = 0;
+  GroupItem item[kMax];
 };
 
 struct SmallPlan {
