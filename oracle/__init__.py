@@ -12,9 +12,12 @@ Contents
   layout    the packed-weight tile layout, written out index by index
   gemm      exact dequantization and the reference product, plus the
             acceptance test used for floating-point parity
+  attention the drafter's symmetric sliding-window attention over a full
+            KV cache (window rule, grouped-query heads, softmax)
 
 Sources: "Quantize the Target, Quantize the Drafter" (arXiv 2607.04244, HTML
-text: the QAD method paragraph and the drafter-PTQ calibration paragraph) and
+text: the QAD method paragraph, the drafter-PTQ calibration paragraph and
+the Drafter SWA paragraph) and
 the Qwen3.5-4B-DFlash-W8A16 model card ("What changed vs upstream" table).
 
 Every function here is pinned by a CPU test against something other than
@@ -22,4 +25,4 @@ itself (closed forms, brute force, library routines, values printed on the
 pages). None is "parity unpinned".
 """
 
-from . import numerics, quant, layout, gemm  # noqa: F401
+from . import numerics, quant, layout, gemm, attention  # noqa: F401

@@ -9,7 +9,8 @@ where it matters.
 import numpy as np
 import pytest
 
-from oracle import gemm, layout, numerics, quant
+from oracle import attention, gemm, layout, numerics, quant
+import test_oracle_attention as ta
 import test_oracle_dequant as td
 import test_oracle_gemm as tg
 import test_oracle_layout as tl
@@ -156,3 +157,53 @@ def test_dequant_truncated_to_bf16_caught(monkeypatch):
         return (x32.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
     monkeypatch.setattr(numerics, "f64_exact_to_bf16", f64_exact_to_bf16)
     _expect_failure(td.test_golden_cases)
+
+
+def _window_variant(kind):
+    def visible_range(seq_len, T, t, window):
+        p = seq_len - T + t
+        full = window == 0 if kind == "no_fallback" else (window == 0 or seq_len <= window)
+        if full:
+            return 0, seq_len
+        half = window // 2
+        if kind == "exclusive":
+            return max(0, p - half + 1), min(seq_len, p + half)
+        if kind == "causal":
+            return max(0, p - window + 1), p + 1
+        if kind == "whole_window_each_side":
+            return max(0, p - window), min(seq_len, p + window + 1)
+        return max(0, p - half), min(seq_len, p + half + 1)
+    return visible_range
+
+
+@pytest.mark.parametrize("kind", ["exclusive", "causal", "no_fallback", "whole_window_each_side"])
+def test_window_mutations_caught(monkeypatch, kind):
+    monkeypatch.setattr(attention, "visible_range", _window_variant(kind))
+    case = {"exclusive": 0, "causal": 0, "no_fallback": 3, "whole_window_each_side": 5}[kind]
+    _expect_failure(ta.test_equal_scores_average_the_window, ta.CASES[case])
+
+
+def _attention_variant(kind):
+    def swa_attention(q, k, v, seq_lens, window, scale):
+        q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
+        B, T, Hq, D = q.shape
+        Hkv = k.shape[2]
+        out = np.zeros((B, T, Hq, D))
+        for b in range(B):
+            S = int(seq_lens[b])
+            for t in range(T):
+                lo, hi = attention.visible_range(S, T, t, window)
+                for h in range(Hq):
+                    kv = h % Hkv if kind == "head_modulo" else h // (Hq // Hkv)
+                    sc = 1.0 if kind == "no_scale" else scale
+                    s_ = (k[b, lo:hi, kv] @ q[b, t, h]) * sc
+                    w = np.exp(s_ - s_.max())
+                    out[b, t, h] = (w / w.sum()) @ v[b, lo:hi, kv]
+        return out
+    return swa_attention
+
+
+@pytest.mark.parametrize("kind", ["head_modulo", "no_scale"])
+def test_attention_mutations_caught(monkeypatch, kind):
+    monkeypatch.setattr(attention, "swa_attention", _attention_variant(kind))
+    _expect_failure(ta.test_full_attention_matches_torch_ragged_batch, 0)

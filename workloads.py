@@ -18,6 +18,12 @@ checkpoint or dataset is used):
     QKV N = 2560 + 2*512 = 3584.
 
 Seeds: 1000*config + 10*shape_index + {0: weights, 1: activations}.
+
+The drafter's sliding-window attention (Drafter SWA paragraph) runs one
+16-token block of queries against a KV cache of the 8,192-token Long context
+plus the block, with a window of 1,024 or 2,048 tokens or none. The head
+layout follows the fused QKV width: 2560 = 20 query heads and 512 = 4 KV heads
+of 128. Seeds: 6000 + 10*case + {0: q, 1: k, 2: v}.
 """
 
 import numpy as np
@@ -33,6 +39,9 @@ WORKLOADS = {
     5: dict(name="prefill_w4a16_m8192", M=8192, bits=4,
             shapes=[(2560, 19456), (9728, 2560)]),
 }
+
+ATTENTION = dict(name="drafter_swa_attention", T=16, Hq=20, Hkv=4, D=128, context=8192,
+                 windows=(1024, 2048, 0))
 
 SHAPE_NAMES = {(2560, 19456): "gate_up", (9728, 2560): "down",
                (2560, 3584): "qkv", (256, 512): "tiny"}
@@ -94,3 +103,14 @@ def scales(G, N, dtype, seed, center=0.0074, spread=0.3):
     if dtype == "f16":
         return s.astype(np.float16).view(np.uint16)
     return to_bf16_bits(s)
+
+
+def attention_inputs(B, T, Hq, Hkv, D, S_max, seed, std=1.0):
+    """q [B, T, Hq, D] and k, v [B, S_max, Hkv, D], each ~ N(0, std) rounded
+    to bf16; returns three uint16 bit-pattern arrays (seeds seed, seed+1,
+    seed+2)."""
+    out = []
+    for i, shape in enumerate(((B, T, Hq, D), (B, S_max, Hkv, D), (B, S_max, Hkv, D))):
+        rng = np.random.default_rng(seed + i)
+        out.append(to_bf16_bits(rng.standard_normal(shape, dtype=np.float32) * np.float32(std)))
+    return tuple(out)
