@@ -268,6 +268,59 @@ qg_status qgemm_w8f16_grouped(const void* x, const qg_group_item* items, int cou
                               qg_dtype s_dt, int64_t M, int64_t K, void* workspace,
                               size_t workspace_bytes, void* stream);
 
+/* Drafter attention with a symmetric sliding window over a full KV cache
+ * ("Quantize the Target, Quantize the Drafter", arXiv 2607.04244, Drafter SWA
+ * paragraph: a fixed window of 1,024 or 2,048 tokens, symmetric around each
+ * query because the drafter's mask-token queries attend bidirectionally,
+ * applied only inside the attention kernel while the cache keeps every
+ * position, and full attention for sequences within the window size; the
+ * drafter setup paragraph fixes a draft block at 16 tokens).
+ *
+ * For each sequence b, its block of T queries sits at cache positions
+ * S_b - T .. S_b - 1, where S_b = seq_lens[b] counts every cache entry of the
+ * sequence, the block's own T included. Query t at position p attends to the
+ * cache positions j < S_b with |p - j| <= window / 2 (integer division), or
+ * to all j < S_b when window == 0 or S_b <= window:
+ *   out[b,t,h,:] = sum_j softmax_j(scale * q[b,t,h,:] . k[b,j,h/G,:]) v[b,j,h/G,:]
+ * with G = Hq / Hkv query heads per KV head.
+ *   q         DEVICE bf16 [B, T, Hq, D]
+ *   k_cache,
+ *   v_cache   DEVICE bf16 [B, S_max, Hkv, D]; rows at or past seq_lens[b]
+ *             are never read
+ *   seq_lens  DEVICE int32 [B]; each must lie in [T, S_max] (values outside
+ *             are clamped into that range, never read out of bounds)
+ *   out       DEVICE bf16 [B, T, Hq, D] (must not alias the inputs)
+ *   D         must be 128; 1 <= T <= 16; Hq % Hkv == 0; window >= 0
+ *   scale     the softmax scale (1/sqrt(D) in the usual model), finite
+ *   workspace qg_swa_workspace_bytes(...) bytes, 16-byte aligned (NULL when
+ *             that is 0); its first 64 KiB are arrival counters that must be
+ *             zero before the first call and are left zero by every call;
+ *             calls that overlap on one workspace race
+ * Softmax and sums in fp32 on the matrix core (probabilities carried as a
+ * bf16 pair, ~2^-18 relative), one rounding to bf16 at the end; identical
+ * inputs give identical bits. Errors: QG_ERR_NULL, QG_ERR_ALIGN (tensors 16
+ * bytes, seq_lens 4), QG_ERR_SHAPE (sizes above, S_max * Hkv * D * 2 or
+ * T * Hq * D * 2 at or past 2^31 bytes, more than 16384 (sequence, head)
+ * pairs for a call that needs the workspace), QG_ERR_WORKSPACE; nothing is
+ * launched on error. B == 0 is a no-op. */
+size_t qg_swa_workspace_bytes(int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t D,
+                              int64_t S_max, int64_t window);
+qg_status qg_swa_attention(const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* seq_lens, void* out, int64_t B, int64_t T,
+                           int64_t Hq, int64_t Hkv, int64_t D, int64_t S_max,
+                           int64_t window, float scale, void* workspace,
+                           size_t workspace_bytes, void* stream);
+/* The same with the number of keys per workgroup chosen by the caller (a
+ * multiple of 32; 0 picks the library's own), for tests and tuning. */
+size_t qg_swa_workspace_bytes_chunk(int64_t B, int64_t T, int64_t Hq, int64_t Hkv,
+                                    int64_t D, int64_t S_max, int64_t window,
+                                    int64_t chunk);
+qg_status qg_swa_attention_chunk(const void* q, const void* k_cache, const void* v_cache,
+                                 const int32_t* seq_lens, void* out, int64_t B, int64_t T,
+                                 int64_t Hq, int64_t Hkv, int64_t D, int64_t S_max,
+                                 int64_t window, float scale, int64_t chunk, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

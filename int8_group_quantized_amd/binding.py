@@ -8,6 +8,7 @@ fallback path.
 """
 
 import ctypes
+import math
 import os
 import threading
 
@@ -69,6 +70,11 @@ _SIGNATURES = {
     "qgemm_w4f16_grouped": ([_P, _ITEMS, _INT, _INT, _I64, _I64, _P, _SZ, _P], _INT),
     "qgemm_w8f16_grouped": ([_P, _ITEMS, _INT, _INT, _I64, _I64, _P, _SZ, _P], _INT),
     "qg_dequant_w8": ([_P, _P, _INT, _I64, _I64, _P, _INT, _P], _INT),
+    "qg_swa_workspace_bytes": ([_I64] * 7, _SZ),
+    "qg_swa_workspace_bytes_chunk": ([_I64] * 8, _SZ),
+    "qg_swa_attention": ([_P, _P, _P, _P, _P] + [_I64] * 7 + [ctypes.c_float, _P, _SZ, _P], _INT),
+    "qg_swa_attention_chunk": ([_P, _P, _P, _P, _P] + [_I64] * 7 + [ctypes.c_float, _I64, _P, _SZ,
+                                                                     _P], _INT),
 }
 
 
@@ -302,3 +308,38 @@ def qgemm_grouped(x, weights, bits, outs=None, ws=None):
     _check(fn, getattr(lib(), fn)(_ptr(x), items, len(weights), _dt(weights[0][1]), M, K,
                                   _ptr(ws), ws_bytes, _stream(x)))
     return outs
+
+
+def swa_attention(q, k_cache, v_cache, seq_lens, window, scale=None, out=None, ws=None, chunk=0):
+    """Drafter attention with a symmetric sliding window over a full KV cache.
+
+    q [B, T, Hq, 128] bf16; k_cache, v_cache [B, S_max, Hkv, 128] bf16;
+    seq_lens int32 [B] on the device (cache entries per sequence, the block's
+    T included); window 0 for full attention. Returns out [B, T, Hq, 128].
+    """
+    _need_cuda(q, k_cache, v_cache, seq_lens)
+    if q.dtype != torch.bfloat16 or k_cache.dtype != torch.bfloat16 or v_cache.dtype != torch.bfloat16:
+        raise TypeError("q, k_cache and v_cache must be bf16")
+    if seq_lens.dtype != torch.int32:
+        raise TypeError("seq_lens must be int32")
+    if not (q.is_contiguous() and k_cache.is_contiguous() and v_cache.is_contiguous()
+            and seq_lens.is_contiguous()):
+        raise ValueError("tensors must be contiguous")
+    B, T, Hq, D = q.shape
+    S_max, Hkv = k_cache.shape[1], k_cache.shape[2]
+    if tuple(k_cache.shape) != (B, S_max, Hkv, D) or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("k_cache / v_cache must both be [B, S_max, Hkv, D]")
+    if seq_lens.shape != (B,):
+        raise ValueError("seq_lens must be [B]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    need = int(lib().qg_swa_workspace_bytes_chunk(B, T, Hq, Hkv, D, S_max, window, chunk))
+    if ws is None and need > 0:
+        ws = workspace(q.device, need)
+    ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
+    _check("qg_swa_attention", lib().qg_swa_attention_chunk(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), _ptr(out), B, T, Hq, Hkv, D, S_max,
+        window, scale, chunk, _ptr(ws), ws_bytes, _stream(q)))
+    return out

@@ -5,6 +5,8 @@
 
 #include <stdint.h>
 
+#include <cmath>
+
 #include "qg_internal.h"
 #include "qgemm.h"
 
@@ -233,6 +235,50 @@ size_t workspace_bytes(int bits, int64_t M, int64_t K, int64_t N, int nbw, int w
   return qg::small_plan_workspace(plan, M, N);
 }
 
+constexpr int64_t kSwaMaxPairs = 65536 / 4;   // arrival counters at the workspace start
+
+qg_status swa_check(int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t D, int64_t S_max,
+                    int64_t window, int64_t chunk, qg::SwaPlan* plan) {
+  if (B < 0 || B > kMaxM || T < 1 || T > 16 || D != 128 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0)
+    return QG_ERR_SHAPE;
+  if (S_max < T || window < 0 || chunk < 0 || chunk % 32 != 0 || chunk > (int64_t(1) << 20))
+    return QG_ERR_SHAPE;
+  if (Hq > 4096 || S_max * Hkv * D * 2 >= kMaxElems || T * Hq * D * 2 >= kMaxElems)
+    return QG_ERR_SHAPE;
+  if (!qg::make_swa_plan(B, T, Hq, Hkv, S_max, window, chunk, plan)) return QG_ERR_SHAPE;
+  if (plan->nchunks > 1 && B * Hq > kSwaMaxPairs) return QG_ERR_SHAPE;
+  if ((int64_t)plan->grid >= kMaxElems) return QG_ERR_SHAPE;
+  return QG_OK;
+}
+
+size_t swa_workspace_bytes(int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t D,
+                           int64_t S_max, int64_t window, int64_t chunk) {
+  qg::SwaPlan plan;
+  if (swa_check(B, T, Hq, Hkv, D, S_max, window, chunk, &plan) != QG_OK || B == 0) return 0;
+  return qg::swa_workspace(plan, B, Hq);
+}
+
+qg_status swa_attention(const void* q, const void* k, const void* v, const int32_t* seq_lens,
+                        void* out, int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t D,
+                        int64_t S_max, int64_t window, float scale, int64_t chunk, void* ws,
+                        size_t ws_bytes, void* stream) {
+  qg::SwaPlan plan;
+  qg_status s = swa_check(B, T, Hq, Hkv, D, S_max, window, chunk, &plan);
+  if (s != QG_OK) return s;
+  if (!(scale == scale) || scale == INFINITY || scale == -INFINITY) return QG_ERR_SHAPE;
+  if (B == 0) return QG_OK;
+  if ((s = check_ptrs({q, k, v, out})) != QG_OK) return s;
+  if (seq_lens == nullptr) return QG_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(seq_lens) & 3u) != 0) return QG_ERR_ALIGN;
+  const size_t need = qg::swa_workspace(plan, B, Hq);
+  if (need > 0) {
+    if (ws == nullptr || ws_bytes < need) return QG_ERR_WORKSPACE;
+    if (!aligned16(ws)) return QG_ERR_ALIGN;
+  }
+  return from_hip(qg::launch_swa_attention(plan, q, k, v, seq_lens, out, T, Hq, Hkv, S_max, scale,
+                                           ws, as_stream(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -415,6 +461,33 @@ qg_status qgemm_w8f16_grouped(const void* x, const qg_group_item* items, int cou
                               int64_t M, int64_t K, void* workspace, size_t workspace_bytes,
                               void* stream) {
   return gemm_grouped(8, true, x, items, count, s_dt, M, K, workspace, workspace_bytes, stream);
+}
+
+size_t qg_swa_workspace_bytes(int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t D,
+                              int64_t S_max, int64_t window) {
+  return swa_workspace_bytes(B, T, Hq, Hkv, D, S_max, window, 0);
+}
+
+qg_status qg_swa_attention(const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* seq_lens, void* out, int64_t B, int64_t T, int64_t Hq,
+                           int64_t Hkv, int64_t D, int64_t S_max, int64_t window, float scale,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  return swa_attention(q, k_cache, v_cache, seq_lens, out, B, T, Hq, Hkv, D, S_max, window,
+                       scale, 0, workspace, workspace_bytes, stream);
+}
+
+size_t qg_swa_workspace_bytes_chunk(int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t D,
+                                    int64_t S_max, int64_t window, int64_t chunk) {
+  return swa_workspace_bytes(B, T, Hq, Hkv, D, S_max, window, chunk);
+}
+
+qg_status qg_swa_attention_chunk(const void* q, const void* k_cache, const void* v_cache,
+                                 const int32_t* seq_lens, void* out, int64_t B, int64_t T,
+                                 int64_t Hq, int64_t Hkv, int64_t D, int64_t S_max,
+                                 int64_t window, float scale, int64_t chunk, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  return swa_attention(q, k_cache, v_cache, seq_lens, out, B, T, Hq, Hkv, D, S_max, window,
+                       scale, chunk, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -94,4 +94,22 @@ hipError_t launch_gemm_small(int bits, const SmallPlan& p, const void* x, bool x
                              const GroupArgs& g, bool s_bf16, int64_t M, int64_t K,
                              void* workspace, hipStream_t st);
 
+// Drafter sliding-window attention (swa_attention.hip): one workgroup per
+// (sequence, query head, chunk of `chunk` keys); `units` = sequences x KV heads
+// x chunks; `window` is 0 when no sequence can exceed it.
+struct SwaPlan {
+  int window = 0;
+  int chunk = 128;
+  int nchunks = 1;
+  int units = 0;
+  int grid = 0;
+};
+bool make_swa_plan(int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t S_max, int64_t window,
+                   int64_t chunk, SwaPlan* p);
+size_t swa_workspace(const SwaPlan& p, int64_t B, int64_t Hq);
+hipError_t launch_swa_attention(const SwaPlan& p, const void* q, const void* k, const void* v,
+                                const int32_t* seq_lens, void* out, int64_t T, int64_t Hq,
+                                int64_t Hkv, int64_t S_max, float scale, void* ws,
+                                hipStream_t st);
+
 }  // namespace qg

@@ -1,0 +1,387 @@
+// Drafter attention with a symmetric sliding window over a full KV cache, for
+// one draft block of up to 16 queries per sequence (gfx950).
+//
+// "Quantize the Target, Quantize the Drafter" (arXiv 2607.04244), Drafter SWA
+// paragraph: the drafter's mask-token queries attend bidirectionally, so the
+// window (1,024 or 2,048 tokens) is symmetric around each query; it exists
+// only inside the attention kernel, the KV cache keeps every position, and a
+// sequence within the window size falls back to full attention. The drafter
+// setup paragraph fixes the block at 16 tokens. Window reading: W // 2
+// positions to each side of the query; the block's queries sit at the last T
+// cache positions; W = 0 is full attention.
+//
+// Work split. A workgroup owns one (sequence, query head, chunk of keys); its
+// four wavefronts take 32-key steps of the chunk in turn and keep an online
+// softmax each. Query heads that share a KV head are dealt to the same XCD
+// (workgroup i runs on XCD i % 8), so their K/V rows come from one L2.
+//
+// Both products run on the bf16 matrix core (16x16x32), transposed so that
+// no probability ever leaves the registers:
+//   S^T = K Q^T   A = K rows (16 keys x 32 dims per lane-row), B = Q^T;
+//                 the result holds, per lane, one query (lane % 16) and four
+//                 keys 4(lane / 16) + e of a 16-key block;
+//   O^T = V^T P^T B = P^T straight from those registers (two 16-key blocks
+//                 give the 8 keys a lane supplies), A = V^T gathered from a
+//                 per-wavefront LDS copy of the step's 32 value rows.
+// P is split into a bf16 high part and the bf16 rounding of the remainder,
+// so P V is accumulated with ~2^-18 relative error in P (two instructions
+// per block) instead of bf16's 2^-9.
+//
+// Chunks of one (sequence, head) are combined deterministically: each
+// workgroup writes (max, sum, unnormalised output) with device-coherent
+// stores, counts its arrival, and the last arrival merges the chunks in
+// chunk order and writes the bf16 output.
+
+#include "qg_internal.h"
+#include "qg_device.h"
+
+#include <cmath>
+
+namespace qg {
+namespace {
+
+constexpr int kD = 128;                        // head dimension
+constexpr int kRowBytes = kD * 2;
+constexpr int kVGroupBytes = 4 * kRowBytes + 32;   // four value rows + pad
+constexpr int kVStageBytes = 8 * kVGroupBytes;     // one step: 32 value rows
+constexpr int kPartFloats = 16 * kD + 32;          // O[16][128], max[16], sum[16]
+constexpr int kWaves = 4;
+constexpr int kCoherent = 16;                  // sc1: bypass the per-XCD L2
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
+__device__ __forceinline__ float xmax(float v, int mask) {
+  return fmaxf(v, __shfl_xor(v, mask));
+}
+
+__global__ __launch_bounds__(256, 2) void swa_attention_kernel(
+    const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* seq_lens,
+    uint16_t* out, uint32_t* counters, float* partials, int T, int Hq, int Hkv, int S_max,
+    int window, float scale_log2, int chunk, int nchunks, int units) {
+  extern __shared__ __align__(16) char lds[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int G = Hq / Hkv;
+  const int xcd = blockIdx.x & 7;
+  const int m = blockIdx.x >> 3;
+  const int u = (m / G) * 8 + xcd;
+  if (u >= units) return;
+  const int hg = m % G;
+  const int c = u % nchunks;
+  const int kvh = (u / nchunks) % Hkv;
+  const int b = u / (nchunks * Hkv);
+  const int h = kvh * G + hg;
+
+  const int S = min(max(seq_lens[b], T), S_max);
+  const bool full = window == 0 || S <= window;
+  const int half = window >> 1;
+  const int p0 = S - T;                          // position of query 0
+  const int lo_u = full ? 0 : max(0, p0 - half);
+  const int hi_u = full ? S : min(S, p0 + T + half);
+  const int k0 = lo_u + c * chunk;
+  const int k1 = min(k0 + chunk, hi_u);
+
+  const int tok = lane & 15;                     // this lane's query (column)
+  const int g = lane >> 4;                       // this lane's key / dim quarter
+  int vlo = 0, vhi = 0;                          // visible keys of the query, in this chunk
+  if (tok < T) {
+    const int p = p0 + tok;
+    vlo = max(full ? 0 : max(0, p - half), k0);
+    vhi = min(full ? S : min(S, p + half + 1), k1);
+  }
+
+  // Q^T operand: query tok, dims 32j + 8g .. +7.
+  const uint32_t kv_seq_bytes = (uint32_t)S * (uint32_t)Hkv * kRowBytes;
+  const uint16_t* kb_ = k + (size_t)b * S_max * Hkv * kD;
+  const uint16_t* vb_ = v + (size_t)b * S_max * Hkv * kD;
+  const __amdgpu_buffer_rsrc_t rk = rsrc(kb_, kv_seq_bytes);
+  const __amdgpu_buffer_rsrc_t rv = rsrc(vb_, kv_seq_bytes);
+  u32x4 bq[4];
+  {
+    const __amdgpu_buffer_rsrc_t rq = rsrc(q + ((size_t)b * T * Hq + h) * kD,
+                                           (uint32_t)(T * Hq * kRowBytes));
+    const uint32_t qoff = (uint32_t)(tok * Hq * kRowBytes + 16 * g);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bq[j] = ld16(rq, tok < T ? qoff + 64 * j : 0x80000000u);
+  }
+
+  const int nsteps = k1 > k0 ? (k1 - k0 + 31) >> 5 : 0;
+  char* vst = lds + wave * kVStageBytes;
+  const uint32_t row_stride = (uint32_t)Hkv * kRowBytes;
+  // K operand rows: key key0 + 16 kb + tok, dims 32j + 8g; value rows for the
+  // LDS stage: key key0 + 4r + g, 16-byte piece tok.
+  const uint32_t k_lane = (uint32_t)tok * row_stride + kvh * kRowBytes + 16 * g;
+  const uint32_t v_lane = (uint32_t)g * row_stride + kvh * kRowBytes + 16 * tok;
+
+  u32x4 kc[2][4], vn[8];
+  auto load_k = [&](u32x4 (&dst)[2][4], int key0) {
+    const uint32_t base = (uint32_t)key0 * row_stride + k_lane;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dst[kb][j] = ld16(rk, base + kb * 16 * row_stride + 64 * j);
+  };
+  auto load_v = [&](int key0) {
+    const uint32_t base = (uint32_t)key0 * row_stride + v_lane;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) vn[r] = ld16(rv, base + 4 * r * row_stride);
+  };
+  auto stage_v = [&]() {
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+      *reinterpret_cast<u32x4*>(vst + r * kVGroupBytes + g * kRowBytes + 16 * tok) = vn[r];
+  };
+
+  float m_run = -INFINITY, l_run = 0.0f;
+  f32x4 o[8];
+#pragma unroll
+  for (int db = 0; db < 8; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  int s = wave;
+  if (s < nsteps) {
+    load_k(kc, k0 + 32 * s);
+    load_v(k0 + 32 * s);
+    stage_v();
+  }
+  // Gather base for V^T: key 4g + i (i < 4) or 16 + 4g + (i - 4), dim 16 db + tok.
+  const uint16_t* vg = reinterpret_cast<const uint16_t*>(vst + g * kVGroupBytes) + tok;
+  for (; s < nsteps; s += kWaves) {
+    const int key0 = k0 + 32 * s;
+    const bool more = s + kWaves < nsteps;
+    u32x4 kn[2][4];
+    if (more) {
+      load_k(kn, key0 + 32 * kWaves);
+      load_v(key0 + 32 * kWaves);
+    }
+    // Scores for two 16-key blocks.
+    float sc[2][4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kc[kb][j]),
+                                                      __builtin_bit_cast(bf16x8, bq[j]), acc, 0,
+                                                      0, 0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int key = key0 + 16 * kb + 4 * g + e;
+        sc[kb][e] = (key >= vlo && key < vhi) ? acc[e] * scale_log2 : -INFINITY;
+        mx = fmaxf(mx, sc[kb][e]);
+      }
+    }
+    mx = xmax(xmax(mx, 16), 32);
+    const float m_new = fmaxf(m_run, mx);
+    const float ms = m_new == -INFINITY ? 0.0f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - ms);
+    float pv[8];
+    float psum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      pv[i] = __builtin_amdgcn_exp2f(sc[i >> 2][i & 3] - ms);
+      psum += pv[i];
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    u32x4 phi, plo;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t hw = pack_bf16x2(pv[2 * w], pv[2 * w + 1]);
+      phi[w] = hw;
+      plo[w] = pack_bf16x2(pv[2 * w] - bf16_bits_to_f32(hw & 0xFFFFu),
+                           pv[2 * w + 1] - bf16_bits_to_f32(hw >> 16));
+    }
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      u32x4 av;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int i0 = 2 * w, i1 = 2 * w + 1;
+        const uint32_t a0 = vg[((i0 >> 2) * 4 * kVGroupBytes + (i0 & 3) * kRowBytes) / 2 + 16 * db];
+        const uint32_t a1 = vg[((i1 >> 2) * 4 * kVGroupBytes + (i1 & 3) * kRowBytes) / 2 + 16 * db];
+        av[w] = a0 | (a1 << 16);
+      }
+      f32x4 od = o[db] * alpha;
+      od = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
+                                                   __builtin_bit_cast(bf16x8, phi), od, 0, 0, 0);
+      o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
+                                                      __builtin_bit_cast(bf16x8, plo), od, 0, 0,
+                                                      0);
+    }
+    if (more) {
+      // The LDS reads above precede these writes in this wavefront's LDS queue.
+      stage_v();
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) kc[kb][j] = kn[kb][j];
+    }
+  }
+  // Sum the lane-partial row sums of a query over the four key quarters.
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+
+  // Merge the four wavefronts in LDS (each reuses its own stage area):
+  // part[16][128] unnormalised output, then max[16], sum[16].
+  float* part = reinterpret_cast<float*>(vst);
+#pragma unroll
+  for (int db = 0; db < 8; ++db)
+    *reinterpret_cast<f32x4*>(part + tok * kD + 16 * db + 4 * g) = o[db];
+  if (g == 0) {
+    part[16 * kD + tok] = m_run;
+    part[16 * kD + 16 + tok] = l_run;
+  }
+  __syncthreads();
+  const int rt = tid >> 4;                         // query of this thread
+  const int d0 = (tid & 15) * 8;                   // its 8 dims
+  float wm[kWaves];
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    wm[w] = reinterpret_cast<const float*>(lds + w * kVStageBytes)[16 * kD + rt];
+    M = fmaxf(M, wm[w]);
+  }
+  const float Ms = M == -INFINITY ? 0.0f : M;
+  float L = 0.0f;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const float* pw = reinterpret_cast<const float*>(lds + w * kVStageBytes);
+    const float f = __builtin_amdgcn_exp2f(wm[w] - Ms);
+    L += f * pw[16 * kD + 16 + rt];
+    const f32x4 a = *reinterpret_cast<const f32x4*>(pw + rt * kD + d0);
+    const f32x4 bb = *reinterpret_cast<const f32x4*>(pw + rt * kD + d0 + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[e] += f * a[e];
+      acc[4 + e] += f * bb[e];
+    }
+  }
+  uint16_t* orow = out + (((size_t)b * T + rt) * Hq + h) * kD + d0;
+  auto store_out = [&](const float (&x)[8], float l) {
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    u32x4 w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(x[2 * e] * inv, x[2 * e + 1] * inv);
+    *reinterpret_cast<u32x4*>(orow) = w;
+  };
+  if (nchunks == 1) {
+    if (rt < T) store_out(acc, L);
+    return;
+  }
+
+  // Split across workgroups: publish this chunk, count the arrival.
+  const size_t pbase = ((size_t)(b * Hq + h) * nchunks) * kPartFloats;
+  const __amdgpu_buffer_rsrc_t rp =
+      rsrc(partials + pbase, (uint32_t)(nchunks * kPartFloats * sizeof(float)));
+  {
+    const uint32_t off = (uint32_t)((c * kPartFloats + rt * kD + d0) * sizeof(float));
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4{__float_as_uint(acc[0]), __float_as_uint(acc[1]),
+                                                 __float_as_uint(acc[2]), __float_as_uint(acc[3])},
+                                           rp, off, 0, kCoherent);
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4{__float_as_uint(acc[4]), __float_as_uint(acc[5]),
+                                                 __float_as_uint(acc[6]), __float_as_uint(acc[7])},
+                                           rp, off + 16, 0, kCoherent);
+    if ((tid & 15) == 0) {
+      const uint32_t moff = (uint32_t)((c * kPartFloats + 16 * kD + rt) * sizeof(float));
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(M), rp, moff, 0, kCoherent);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(L), rp, moff + 64, 0, kCoherent);
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  __shared__ uint32_t s_last;
+  const int cidx = b * Hq + h;
+  if (tid == 0) {
+    const uint32_t prev =
+        __hip_atomic_fetch_add(&counters[cidx], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = prev == (uint32_t)nchunks - 1u ? 1u : 0u;
+  }
+  __syncthreads();
+  if (s_last == 0u) return;
+
+  // Last arrival: merge every chunk in chunk order.
+  float Mx = -INFINITY;
+  for (int cc = 0; cc < nchunks; ++cc) {
+    const uint32_t moff = (uint32_t)((cc * kPartFloats + 16 * kD + rt) * sizeof(float));
+    Mx = fmaxf(Mx, __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, moff, 0, kCoherent)));
+  }
+  const float Mxs = Mx == -INFINITY ? 0.0f : Mx;
+  float tot[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float Lt = 0.0f;
+  for (int cc = 0; cc < nchunks; ++cc) {
+    const uint32_t base = (uint32_t)(cc * kPartFloats * sizeof(float));
+    const uint32_t moff = base + (uint32_t)((16 * kD + rt) * sizeof(float));
+    const float mc = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, moff, 0, kCoherent));
+    const float lc =
+        __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, moff + 64, 0, kCoherent));
+    const uint32_t off = base + (uint32_t)((rt * kD + d0) * sizeof(float));
+    const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rp, off, 0, kCoherent);
+    const u32x4 bb = __builtin_amdgcn_raw_buffer_load_b128(rp, off + 16, 0, kCoherent);
+    const float f = __builtin_amdgcn_exp2f(mc - Mxs);
+    Lt += f * lc;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      tot[e] += f * __uint_as_float(a[e]);
+      tot[4 + e] += f * __uint_as_float(bb[e]);
+    }
+  }
+  if (rt < T) store_out(tot, Lt);
+  if (tid == 0)   // ready for the next call on this workspace
+    __hip_atomic_store(&counters[cidx], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace
+
+bool make_swa_plan(int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t S_max, int64_t window,
+                   int64_t chunk_req, SwaPlan* p) {
+  const int64_t w = window >= S_max ? 0 : window;   // a window past every sequence is no window
+  const int64_t span = w == 0 ? S_max : std::min<int64_t>(S_max, w + T);
+  // Aim for about two workgroups per CU over the whole call, with at least
+  // four 32-key steps (one per wavefront) per chunk.
+  const int64_t heads = std::max<int64_t>(1, B * Hq);
+  const int64_t target = std::max<int64_t>(1, std::min<int64_t>(32, (512 + heads - 1) / heads));
+  int64_t chunk = (span + target - 1) / target;
+  chunk = std::max<int64_t>(128, (chunk + 31) / 32 * 32);
+  if (chunk_req > 0) chunk = chunk_req;
+  p->window = (int)w;
+  p->chunk = (int)chunk;
+  p->nchunks = (int)((span + chunk - 1) / chunk);
+  const int64_t units = B * Hkv * p->nchunks;
+  p->units = (int)units;
+  p->grid = (int)(8 * (Hq / Hkv) * ((units + 7) / 8));
+  return units < (1 << 24);
+}
+
+size_t swa_workspace(const SwaPlan& p, int64_t B, int64_t Hq) {
+  if (p.nchunks <= 1) return 0;
+  return (size_t)kCounterBytes + (size_t)B * Hq * p.nchunks * kPartFloats * sizeof(float);
+}
+
+hipError_t launch_swa_attention(const SwaPlan& p, const void* q, const void* k, const void* v,
+                                const int32_t* seq_lens, void* out, int64_t T, int64_t Hq,
+                                int64_t Hkv, int64_t S_max, float scale, void* ws,
+                                hipStream_t st) {
+  uint32_t* counters = nullptr;
+  float* partials = nullptr;
+  if (p.nchunks > 1) {
+    counters = static_cast<uint32_t*>(ws);
+    partials = reinterpret_cast<float*>(static_cast<char*>(ws) + kCounterBytes);
+  }
+  const float scale_log2 = (float)((double)scale * 1.4426950408889634);
+  swa_attention_kernel<<<p.grid, 64 * kWaves, kWaves * kVStageBytes, st>>>(
+      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+      static_cast<const uint16_t*>(v), seq_lens, static_cast<uint16_t*>(out), counters, partials,
+      (int)T, (int)Hq, (int)Hkv, (int)S_max, p.window, scale_log2, p.chunk, p.nchunks, p.units);
+  return hipGetLastError();
+}
+
+}  // namespace qg

@@ -182,3 +182,53 @@ def test_grouped_entry_points_validate():
     assert L.qg_workspace_bytes_grouped(4, 16, 9728, _items(2560), 1) == \
         L.qg_workspace_bytes(4, 16, 9728, 2560)
     assert L.qg_workspace_bytes_grouped(4, 16, 9728, None, 1) == 0
+
+
+def _swa(L, B=1, T=16, Hq=20, Hkv=4, D=128, S_max=8208, window=1024, scale=0.088, chunk=0,
+         q=FAKE, k=FAKE, v=FAKE, lens=FAKE, out=FAKE, ws=FAKE, ws_bytes=1 << 30):
+    return L.qg_swa_attention_chunk(q, k, v, lens, out, B, T, Hq, Hkv, D, S_max, window, scale,
+                                    chunk, ws, ws_bytes, None)
+
+
+def test_swa_attention_validates():
+    L = q.lib()
+    # shapes
+    assert _swa(L, D=64) == SHAPE
+    assert _swa(L, T=0) == SHAPE
+    assert _swa(L, T=17) == SHAPE
+    assert _swa(L, Hq=20, Hkv=3) == SHAPE
+    assert _swa(L, Hkv=0) == SHAPE
+    assert _swa(L, S_max=8) == SHAPE                # shorter than the block
+    assert _swa(L, window=-1) == SHAPE
+    assert _swa(L, chunk=48) == SHAPE               # not a multiple of 32
+    assert _swa(L, B=-1) == SHAPE
+    assert _swa(L, S_max=1 << 22, Hkv=16) == SHAPE  # a sequence's cache past 2^31 bytes
+    assert _swa(L, scale=float("nan")) == SHAPE
+    assert _swa(L, scale=float("inf")) == SHAPE
+    # pointers
+    assert _swa(L, q=0) == NULL
+    assert _swa(L, lens=0) == NULL
+    assert _swa(L, out=MIS) == ALIGN
+    assert _swa(L, lens=FAKE + 2) == ALIGN
+    # workspace (the library plan splits S = 8208 into chunks)
+    need = L.qg_swa_workspace_bytes(1, 16, 20, 4, 128, 8208, 1024)
+    assert need > 65536
+    assert _swa(L, ws=0, ws_bytes=0) == WS
+    assert _swa(L, ws_bytes=need - 1) == WS
+    assert _swa(L, ws=MIS) == ALIGN
+    # an empty batch is a no-op that touches nothing
+    assert _swa(L, B=0, q=0, k=0, v=0, lens=0, out=0, ws=0, ws_bytes=0) == OK
+
+
+def test_swa_workspace_sizes():
+    L = q.lib()
+    # one chunk (a short cache, or a chunk covering the whole window) needs none
+    assert L.qg_swa_workspace_bytes(1, 16, 20, 4, 128, 100, 0) == 0
+    assert L.qg_swa_workspace_bytes_chunk(1, 16, 20, 4, 128, 8208, 1024, 2048) == 0
+    # otherwise the counter block plus per-chunk partials (16 x 128 outputs,
+    # 16 maxima, 16 sums, fp32) for each (sequence, query head)
+    n = L.qg_swa_workspace_bytes_chunk(2, 16, 8, 2, 128, 1000, 0, 256)
+    assert n == 65536 + 2 * 8 * 4 * (16 * 128 + 32) * 4
+    # a window wider than the cache is no window
+    assert L.qg_swa_workspace_bytes(1, 16, 20, 4, 128, 1000, 5000) == \
+        L.qg_swa_workspace_bytes(1, 16, 20, 4, 128, 1000, 0)

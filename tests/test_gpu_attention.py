@@ -1,0 +1,132 @@
+"""GPU parity for the drafter's sliding-window attention (Drafter SWA
+paragraph of arXiv 2607.04244) against the oracle's float64 definition.
+
+Acceptance, per output element of one call:
+    |gpu - ref| <= 1e-2 |ref| + 1e-3 rms(ref),
+ref in float64 before output rounding. The kernel's own error is far inside
+it: scores are fp32 sums of exact bf16 products, the softmax runs in fp32,
+probabilities enter the value product as a bf16 pair (~2^-18 relative), the
+sums are fp32, and the one bf16 rounding of the output is 2^-9 relative.
+
+Inputs: q, k, v ~ N(0, 1) rounded to bf16, seeded; the drafter's head layout
+(20 query heads, 4 KV heads of 128) and a 16-token block over the 8,192-token
+Long context, plus smaller ragged batches.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import int8_group_quantized_amd as q
+from oracle import attention, numerics
+import workloads
+from gpu_helpers import DEV, dev_bf16, host_u16
+
+pytestmark = pytest.mark.gpu
+
+D = 128
+
+
+def _run(B, T, Hq, Hkv, S_max, lens, window, seed, scale=None, chunk=0, std=1.0, poison=False):
+    qb, kb, vb = workloads.attention_inputs(B, T, Hq, Hkv, D, S_max, seed, std=std)
+    if poison:   # NaN past each sequence's end: must never be read
+        for b, S in enumerate(lens):
+            kb[b, min(max(S, T), S_max):] = 0x7FC0
+            vb[b, min(max(S, T), S_max):] = 0x7FC0
+    sc = 1.0 / np.sqrt(D) if scale is None else scale
+    out = q.swa_attention(dev_bf16(qb), dev_bf16(kb), dev_bf16(vb),
+                          torch.tensor(lens, dtype=torch.int32, device=DEV), window, sc,
+                          chunk=chunk)
+    torch.cuda.synchronize()
+    return qb, kb, vb, sc, host_u16(out)
+
+
+def _ref(qb, kb, vb, lens, T, S_max, window, sc):
+    eff = [min(max(S, T), S_max) for S in lens]
+    return attention.swa_attention(numerics.bf16_to_f64(qb), numerics.bf16_to_f64(kb),
+                                   numerics.bf16_to_f64(vb), eff, window, sc)
+
+
+def _check(got_bits, ref, what=""):
+    got = numerics.bf16_to_f64(got_bits)
+    assert np.isfinite(got).all(), what
+    rms = np.sqrt(np.mean(ref ** 2))
+    err = np.abs(got - ref)
+    bound = 1e-2 * np.abs(ref) + 1e-3 * rms
+    bad = np.argwhere(err > bound)
+    assert bad.size == 0, "%s: %d bad, first %s got %r ref %r" % (
+        what, len(bad), bad[0], got[tuple(bad[0])], ref[tuple(bad[0])])
+
+
+def _parity(B, T, Hq, Hkv, S_max, lens, window, seed, **kw):
+    print("swa case B=%d T=%d Hq=%d Hkv=%d S_max=%d lens=%s window=%d %s" %
+          (B, T, Hq, Hkv, S_max, lens, window, kw), flush=True)
+    qb, kb, vb, sc, got = _run(B, T, Hq, Hkv, S_max, lens, window, seed, **kw)
+    ref = _ref(qb, kb, vb, lens, T, S_max, window, sc)
+    _check(got, ref, "B%d T%d S%s W%d" % (B, T, lens, window))
+    return got
+
+
+@pytest.mark.parametrize("window", [1024, 2048, 0])
+def test_drafter_long_context_full_size(window):
+    # one 16-token block after the 8,192-token Long context, drafter heads
+    A = workloads.ATTENTION
+    S = A["context"] + A["T"]
+    _parity(1, A["T"], A["Hq"], A["Hkv"], S, [S], window, 6000 + window)
+
+
+@pytest.mark.parametrize("window", [0, 64, 256, 1024, 5, 1])
+def test_ragged_batch(window):
+    # a long sequence, a medium one, one that is only the block, and one
+    # just past the window
+    _parity(4, 16, 8, 2, 700, [700, 333, 16, 65], window, 6100 + window)
+
+
+@pytest.mark.parametrize("T", [1, 7, 15])
+def test_partial_blocks(T):
+    _parity(2, T, 20, 4, 1500, [1500, 900], 1024, 6200 + T)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (8, 1), (16, 2)])
+def test_head_layouts(Hq, Hkv):
+    _parity(2, 16, Hq, Hkv, 1200, [1200, 1037], 512, 6300 + Hq * 10 + Hkv)
+
+
+@pytest.mark.parametrize("chunk", [32, 64, 96, 4096])
+def test_explicit_chunks(chunk):
+    # 32: one step per workgroup (three wavefronts idle, many chunks to merge);
+    # 4096: the whole window in one workgroup (no cross-workgroup merge)
+    _parity(2, 16, 20, 4, 3000, [3000, 2100], 2048, 6400 + chunk, chunk=chunk)
+
+
+def test_seq_lens_are_clamped():
+    # a length past the cache reads as S_max, one below the block as T
+    _parity(2, 4, 4, 2, 300, [400, 2], 64, 6500)
+
+
+def test_cache_past_sequence_end_is_not_read():
+    lens = [900, 417, 16]
+    _, _, _, _, clean = _run(3, 16, 20, 4, 1000, lens, 256, 6600)
+    _, _, _, _, dirty = _run(3, 16, 20, 4, 1000, lens, 256, 6600, poison=True)
+    np.testing.assert_array_equal(dirty, clean)
+
+
+@pytest.mark.parametrize("scale,std", [(0.05, 1.0), (1.0, 1.0), (1.0 / np.sqrt(128), 4.0)])
+def test_scales_and_sharp_softmax(scale, std):
+    _parity(1, 16, 20, 4, 2000, [2000], 1024, 6700, scale=scale, std=std)
+
+
+def test_deterministic_and_workspace_reusable():
+    lens = [2500, 1800]
+    a = _parity(2, 16, 20, 4, 2500, lens, 0, 6800)
+    for _ in range(3):
+        _, _, _, _, b = _run(2, 16, 20, 4, 2500, lens, 0, 6800)
+        np.testing.assert_array_equal(a, b)
+
+
+def test_empty_batch_is_a_no_op():
+    qt = torch.empty((0, 16, 20, D), dtype=torch.bfloat16, device=DEV)
+    kt = torch.empty((0, 100, 4, D), dtype=torch.bfloat16, device=DEV)
+    lens = torch.empty((0,), dtype=torch.int32, device=DEV)
+    out = q.swa_attention(qt, kt, kt, lens, 0)
+    assert out.shape == qt.shape
