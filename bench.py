@@ -17,7 +17,9 @@ Besides the headline line, the same JSON object carries
   roofline      the dominant kernel (gate/up GEMV), timed live with events;
   cpu_baseline  the CPU oracle timed on a bounded sample of the same step;
   workloads     the other shapes (M=16 verification, W8A16 drafter, M=8192
-                prefill, Q_s packing), each with its roofline fraction.
+                prefill, fp16 activations, Q_s packing, dense dequantization,
+                the fake quantizer, the grouped K+V launch, and the drafter's
+                sliding-window attention), each with its roofline fraction.
 """
 
 import argparse
@@ -322,6 +324,42 @@ def measure_grouped(torch, q, bits):
             "gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
 
 
+def measure_attention(torch, q, window, B=1):
+    """The drafter's sliding-window attention for one 16-token block after the
+    8,192-token Long context (20 query heads, 4 KV heads of 128), over
+    rotating copies of the KV cache so the window rows come from HBM."""
+    import workloads
+    A = workloads.ATTENTION
+    T, Hq, Hkv, D = A["T"], A["Hq"], A["Hkv"], A["D"]
+    S = A["context"] + T
+    lo = 0 if (window == 0 or S <= window) else max(0, S - T - window // 2)
+    kv_read = B * (S - lo) * Hkv * D * 2 * 2           # K and V rows any query sees
+    nbytes = kv_read + 2 * B * T * Hq * D * 2           # + q and out
+    copies = max(1, math.ceil(2 * MALL_BYTES / kv_read))
+    qb, kb, vb = workloads.attention_inputs(B, T, Hq, Hkv, D, S, 6900)
+    bf = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    qt, kt, vt = bf(qb), bf(kb), bf(vb)
+    k_all = torch.empty((copies, B, S, Hkv, D), dtype=torch.bfloat16, device="cuda")
+    v_all = torch.empty_like(k_all)
+    k_all[:, :, lo:] = kt[:, lo:]                      # rows before lo are never read
+    v_all[:, :, lo:] = vt[:, lo:]
+    lens = torch.full((B,), S, dtype=torch.int32, device="cuda")
+    out = torch.empty_like(qt)
+    ws = torch.zeros(max(1, q.lib().qg_swa_workspace_bytes(B, T, Hq, Hkv, D, S, window)),
+                     dtype=torch.uint8, device="cuda")
+    g = capture(torch, lambda i: q.swa_attention(qt, k_all[i % copies], v_all[i % copies], lens,
+                                                 window, out=out, ws=ws), 100)
+    g.replay()
+    us = time_graphs(torch, [g], reps=4) / 400 * 1e3
+    del g, k_all, v_all
+    torch.cuda.empty_cache()
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"workload": "drafter attention, 16-token block over 8192 + 16 cached tokens, "
+                        "window %s, batch %d" % (window if window else "none (full)", B),
+            "us_per_call": round(us, 2), "bytes_per_call": nbytes, "gbs": round(gbs, 1),
+            "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "cache_copies": copies}
+
+
 def cpu_baseline(seconds):
     """The oracle's product for the headline step, timed on the host."""
     from oracle import gemm, numerics, quant
@@ -408,6 +446,9 @@ def main():
         extra.append(measure_fake_quant(torch, q))
         extra.append(measure_grouped(torch, q, 8))
         extra.append(measure_grouped(torch, q, 4))
+        for B in (1, 8):
+            for w in (1024, 2048, 0):
+                extra.append(measure_attention(torch, q, w, B))
 
     if args.copy_calibration:
         copy_calibration(torch)

@@ -44,8 +44,13 @@ constexpr int kD = 128;                        // head dimension
 constexpr int kRowBytes = kD * 2;
 constexpr int kVGroupBytes = 4 * kRowBytes + 32;   // four value rows + pad
 constexpr int kVStageBytes = 8 * kVGroupBytes;     // one step: 32 value rows
-constexpr int kPartFloats = 16 * kD + 32;          // O[16][128], max[16], sum[16]
 constexpr int kWaves = 4;
+constexpr int kWavesLds = kWaves * kVStageBytes;
+constexpr int kOFloats = 16 * kD;                  // one chunk's O[16][128]
+constexpr int kPartFloats = kOFloats + 32;         // + max[16], sum[16]
+constexpr int kMaxChunks = 256;   // merge table of maxima and sums in LDS (128 B per chunk)
+static_assert(kMaxChunks * 128 <= kWavesLds, "merge table exceeds the LDS stage area");
+static_assert(kMaxChunks * 8 % (64 * kWaves) == 0, "merge table loads");
 constexpr int kCoherent = 16;                  // sc1: bypass the per-XCD L2
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
@@ -85,8 +90,11 @@ __global__ __launch_bounds__(256, 2) void swa_attention_kernel(
   const int p0 = S - T;                          // position of query 0
   const int lo_u = full ? 0 : max(0, p0 - half);
   const int hi_u = full ? S : min(S, p0 + T + half);
-  const int k0 = lo_u + c * chunk;
-  const int k1 = min(k0 + chunk, hi_u);
+  // The sequence's own span is divided evenly among the chunks (a short
+  // sequence or a window cut by the cache end leaves no chunk empty).
+  const int per = min(chunk, (hi_u - lo_u + nchunks - 1) / nchunks);
+  const int k0 = min(lo_u + c * per, hi_u);
+  const int k1 = min(k0 + per, hi_u);
 
   const int tok = lane & 15;                     // this lane's query (column)
   const int g = lane >> 4;                       // this lane's key / dim quarter
@@ -278,12 +286,15 @@ __global__ __launch_bounds__(256, 2) void swa_attention_kernel(
     return;
   }
 
-  // Split across workgroups: publish this chunk, count the arrival.
+  // Split across workgroups: publish this chunk, count the arrival. The
+  // region of one (sequence, head) holds every chunk's O[16][128], then every
+  // chunk's max[16] and sum[16], so the merge reads the maxima in one sweep.
   const size_t pbase = ((size_t)(b * Hq + h) * nchunks) * kPartFloats;
+  const uint32_t ml0 = (uint32_t)(nchunks * kOFloats * sizeof(float));
   const __amdgpu_buffer_rsrc_t rp =
       rsrc(partials + pbase, (uint32_t)(nchunks * kPartFloats * sizeof(float)));
   {
-    const uint32_t off = (uint32_t)((c * kPartFloats + rt * kD + d0) * sizeof(float));
+    const uint32_t off = (uint32_t)((c * kOFloats + rt * kD + d0) * sizeof(float));
     __builtin_amdgcn_raw_buffer_store_b128(u32x4{__float_as_uint(acc[0]), __float_as_uint(acc[1]),
                                                  __float_as_uint(acc[2]), __float_as_uint(acc[3])},
                                            rp, off, 0, kCoherent);
@@ -291,7 +302,7 @@ __global__ __launch_bounds__(256, 2) void swa_attention_kernel(
                                                  __float_as_uint(acc[6]), __float_as_uint(acc[7])},
                                            rp, off + 16, 0, kCoherent);
     if ((tid & 15) == 0) {
-      const uint32_t moff = (uint32_t)((c * kPartFloats + 16 * kD + rt) * sizeof(float));
+      const uint32_t moff = ml0 + (uint32_t)((c * 32 + rt) * sizeof(float));
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(M), rp, moff, 0, kCoherent);
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(L), rp, moff + 64, 0, kCoherent);
     }
@@ -308,30 +319,58 @@ __global__ __launch_bounds__(256, 2) void swa_attention_kernel(
   __syncthreads();
   if (s_last == 0u) return;
 
-  // Last arrival: merge every chunk in chunk order.
-  float Mx = -INFINITY;
-  for (int cc = 0; cc < nchunks; ++cc) {
-    const uint32_t moff = (uint32_t)((cc * kPartFloats + 16 * kD + rt) * sizeof(float));
-    Mx = fmaxf(Mx, __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, moff, 0, kCoherent)));
+  // Last arrival: merge every chunk in chunk order. Maxima and sums of all
+  // chunks go to LDS in one sweep of 16-byte loads; the outputs follow in
+  // batches of eight chunks whose loads are all in flight together (a slot
+  // past the last chunk reads zeros through the buffer range check).
+  float* ml = reinterpret_cast<float*>(lds);
+  constexpr int kBatch = 8;
+  u32x4 a[kBatch], bb[kBatch];
+  auto issue = [&](int c0) {
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const uint32_t off = c0 + i < nchunks
+                               ? (uint32_t)(((c0 + i) * kOFloats + rt * kD + d0) * sizeof(float))
+                               : 0x80000000u;
+      a[i] = __builtin_amdgcn_raw_buffer_load_b128(rp, off, 0, kCoherent);
+      bb[i] = __builtin_amdgcn_raw_buffer_load_b128(rp, off + 16, 0, kCoherent);
+    }
+  };
+  // The first batch of outputs and the whole table of maxima and sums are in
+  // flight together.
+  u32x4 mlv[kMaxChunks * 8 / (64 * kWaves)];
+  constexpr int kMlPer = kMaxChunks * 8 / (64 * kWaves);
+  __syncthreads();                                 // the wavefront merge above is done
+#pragma unroll
+  for (int j = 0; j < kMlPer; ++j) {
+    const int i = tid + j * 64 * kWaves;
+    mlv[j] = __builtin_amdgcn_raw_buffer_load_b128(
+        rp, i < nchunks * 8 ? ml0 + 16 * i : 0x80000000u, 0, kCoherent);
+    if (j == 0) issue(0);
   }
+#pragma unroll
+  for (int j = 0; j < kMlPer; ++j) {
+    const int i = tid + j * 64 * kWaves;
+    if (i < nchunks * 8) *reinterpret_cast<u32x4*>(ml + 4 * i) = mlv[j];
+  }
+  __syncthreads();
+  float Mx = -INFINITY;
+  for (int cc = 0; cc < nchunks; ++cc) Mx = fmaxf(Mx, ml[cc * 32 + rt]);
   const float Mxs = Mx == -INFINITY ? 0.0f : Mx;
   float tot[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float Lt = 0.0f;
-  for (int cc = 0; cc < nchunks; ++cc) {
-    const uint32_t base = (uint32_t)(cc * kPartFloats * sizeof(float));
-    const uint32_t moff = base + (uint32_t)((16 * kD + rt) * sizeof(float));
-    const float mc = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, moff, 0, kCoherent));
-    const float lc =
-        __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, moff + 64, 0, kCoherent));
-    const uint32_t off = base + (uint32_t)((rt * kD + d0) * sizeof(float));
-    const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rp, off, 0, kCoherent);
-    const u32x4 bb = __builtin_amdgcn_raw_buffer_load_b128(rp, off + 16, 0, kCoherent);
-    const float f = __builtin_amdgcn_exp2f(mc - Mxs);
-    Lt += f * lc;
+  for (int c0 = 0; c0 < nchunks; c0 += kBatch) {
+    if (c0 > 0) issue(c0);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      tot[e] += f * __uint_as_float(a[e]);
-      tot[4 + e] += f * __uint_as_float(bb[e]);
+    for (int i = 0; i < kBatch; ++i) {
+      const int cc = min(c0 + i, nchunks - 1);
+      const float f = c0 + i < nchunks ? __builtin_amdgcn_exp2f(ml[cc * 32 + rt] - Mxs) : 0.0f;
+      Lt += f * ml[cc * 32 + 16 + rt];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        tot[e] += f * __uint_as_float(a[i][e]);
+        tot[4 + e] += f * __uint_as_float(bb[i][e]);
+      }
     }
   }
   if (rt < T) store_out(tot, Lt);
@@ -344,19 +383,25 @@ __global__ __launch_bounds__(256, 2) void swa_attention_kernel(
 bool make_swa_plan(int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t S_max, int64_t window,
                    int64_t chunk_req, SwaPlan* p) {
   const int64_t w = window >= S_max ? 0 : window;   // a window past every sequence is no window
-  const int64_t span = w == 0 ? S_max : std::min<int64_t>(S_max, w + T);
-  // Aim for about two workgroups per CU over the whole call, with at least
-  // four 32-key steps (one per wavefront) per chunk.
+  // Longest key span of any sequence: the whole cache without a window; else
+  // a sequence within the window (full attention, at most W keys) or the
+  // block plus W / 2 keys before its first query.
+  const int64_t span = w == 0 ? S_max : std::min<int64_t>(S_max, std::max<int64_t>(w, T + w / 2));
+  // About 384 workgroups over the whole call (a sweep of chunk sizes over the
+  // drafter's Long-context shapes at batch 1 and 8), and at least 256 keys
+  // (two 32-key steps per wavefront) per chunk: a cross-workgroup merge costs
+  // more than a short chunk saves.
   const int64_t heads = std::max<int64_t>(1, B * Hq);
-  const int64_t target = std::max<int64_t>(1, std::min<int64_t>(32, (512 + heads - 1) / heads));
+  const int64_t target = std::max<int64_t>(1, std::min<int64_t>(64, (384 + heads - 1) / heads));
   int64_t chunk = (span + target - 1) / target;
-  chunk = std::max<int64_t>(128, (chunk + 31) / 32 * 32);
+  chunk = std::max<int64_t>(256, (chunk + 31) / 32 * 32);
   if (chunk_req > 0) chunk = chunk_req;
   p->window = (int)w;
   p->chunk = (int)chunk;
   p->nchunks = (int)((span + chunk - 1) / chunk);
   const int64_t units = B * Hkv * p->nchunks;
   p->units = (int)units;
+  if (p->nchunks > kMaxChunks) return false;
   p->grid = (int)(8 * (Hq / Hkv) * ((units + 7) / 8));
   return units < (1 << 24);
 }
