@@ -112,6 +112,7 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_small_kernel(
   constexpr int TW = Tile<BITS>::words;
   constexpr int D = Batch<BITS, NBW>::D;
   constexpr int XG = (MR == 1) ? 16 : 256;   // LDS 16-byte words of x per group
+  constexpr int CBW = WN * NBW;               // column blocks of the workgroup
   using A = Act<XH>;
   extern __shared__ u32x4 smem[];
 
@@ -146,13 +147,15 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_small_kernel(
   const int l16 = lane & 15;                 // A row / C column of this lane
   const int lq = lane >> 4;                  // K slice (A, B) / row quad (C)
   u32x4* xs = smem;                          // [sg][XG] x fragments, then a zero block (MR == 1)
+  // The scales of the workgroup's column blocks and groups follow: 32 bytes
+  // (16 columns) per (column block, group), [CBW][sn] order.
+  u32x4* ss = smem + sg * XG + 16;
   const uint32_t magic = opaque_magic(A::kMagic);
 
   int cb[NBW];
 #pragma unroll
   for (int c = 0; c < NBW; ++c) cb[c] = min(cb0 + c, NB - 1);   // clamped: stays in range
   const int lane_off = lane * (TB / 64);
-  const int s_off = l16 * 2;                 // this lane's scale within a tile's 16
   // x fragment address of this lane for stage group 0, and its per-group step
   // (in 16-byte words); with MR == 1 only lanes of row 0 read data, the rest
   // read the zero block.
@@ -174,31 +177,26 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_small_kernel(
     const int nbatch = (w_n + D - 1) / D;
 
     u32x4 ta[D][NBW][TW], tb[D][NBW][TW];
-    uint32_t sa[D][NBW], sb[D][NBW];
-    // Batch b: groups g_first + b*D + d of each column block, through
-    // resources that end at the wavefront's last group (later ones read 0):
-    // the tiles, and the 16 scales of each tile (one per lane column).
-    auto load_batch = [&](int b, u32x4 (&t)[D][NBW][TW], uint32_t (&sc)[D][NBW]) {
+    const uint16_t* ssc = reinterpret_cast<const uint16_t*>(ss);
+    // Batch b: groups g_first + b*D + d of each column block, through a
+    // resource that ends at the wavefront's last group (later ones read 0).
+    auto load_batch = [&](int b, u32x4 (&t)[D][NBW][TW]) {
       const int i0 = min(b * D, w_n);
       const int left = w_n - i0;                      // groups still in range
 #pragma unroll
       for (int c = 0; c < NBW; ++c) {
         const __amdgpu_buffer_rsrc_t r =
             make_rsrc(packed + ((int64_t)cb[c] * G + g_first + i0) * TB, left * TB);
-        const __amdgpu_buffer_rsrc_t rs =
-            make_rsrc(scales + (int64_t)(g_first + i0) * N + cb[c] * 16,
-                      left > 0 ? (left - 1) * N * 2 + 32 : 0);
 #pragma unroll
         for (int d = 0; d < D; ++d) {
 #pragma unroll
           for (int v = 0; v < TW; ++v)
             t[d][c][v] = __builtin_bit_cast(
                 u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, lane_off + d * TB + 16 * v, 0, 0));
-          sc[d][c] = __builtin_amdgcn_raw_buffer_load_b16(rs, s_off + d * N * 2, 0, 0);
         }
       }
     };
-    auto compute_batch = [&](int b, const u32x4 (&t)[D][NBW][TW], const uint32_t (&sc)[D][NBW]) {
+    auto compute_batch = [&](int b, const u32x4 (&t)[D][NBW][TW]) {
 #pragma unroll
       for (int d = 0; d < D; ++d) {
         const int i = b * D + d;                      // wave-relative group
@@ -227,7 +225,7 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_small_kernel(
             p = A::mma(a[2], int8_words_to_act<A>(t[d][c][1][0], t[d][c][1][1]), p);
             p = A::mma(a[3], int8_words_to_act<A>(t[d][c][1][2], t[d][c][1][3]), p);
           }
-          const uint32_t sbits = sc[d][c];
+          const uint32_t sbits = ssc[((wn * NBW + c) * sn + gl) * 16 + l16];
           const float sv = SBF ? bf16_bits_to_f32(sbits) : f16_bits_to_f32(sbits);
           const float scale = live ? sv : 0.0f;
           if constexpr (MR == 1) {
@@ -273,36 +271,73 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_small_kernel(
               src, (__attribute__((address_space(3))) void*)(xs + w0), 16, 0, 0);
         }
       }
+      // The scales, 16 bytes (8 columns) per lane: one sweep per workgroup
+      // instead of a load per tile in every wavefront.
+      const int stotal = CBW * sn * 2;
+      for (int w0 = wave * 64; w0 < stotal; w0 += NW * 64) {
+        const int e = w0 + lane;
+        if (e < stotal) {
+          const int cc = e / (2 * sn);
+          const int rem = e - cc * 2 * sn;
+          const int cbw = min(((int)blockIdx.x - wg0) * CBW + cc, NB - 1);
+          const uint16_t* src = scales + (int64_t)(wg_g0 + s0 + (rem >> 1)) * N + cbw * 16 +
+                                8 * (rem & 1);
+          __builtin_amdgcn_global_load_lds(
+              src, (__attribute__((address_space(3))) void*)(ss + w0), 16, 0, 0);
+        }
+      }
     }
-    // Both tile batches go out after the staging loads (the empty asm keeps
-    // the compiler from hoisting them); waiting until no more than their
-    // count is outstanding then waits for the staging only, and the zero
-    // slots written through LDS are complete before the barrier.
+    // The first tile batches go out after the staging loads (the empty asm
+    // keeps the compiler from hoisting them); waiting until no more than
+    // their count is outstanding then waits for the staging only, and the
+    // zero slots written through LDS are complete before the barrier.
+    // A fetch past the wavefront's last group reads zeros without touching
+    // memory but still occupies the address unit like a real one, so one and
+    // two batches (the common decode and verification shapes) take
+    // straight-line paths that issue nothing beyond them; longer runs use the
+    // pairwise pipeline, whose last pair fetches ahead past the end. Each
+    // path has static wait counts (a load issued on only some paths would
+    // make the compiler drain every load before each use).
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
-    load_batch(0, ta, sa);
-    load_batch(1, tb, sb);
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * D * NBW * (TW + 1)));
-    asm volatile("s_barrier" ::: "memory");
-
-    if (w_n > 0) {
-      // Batches in pairs: multiply one while the other is in flight. The loop
-      // body is straight-line code (fetches past the wave's last group return
-      // zeros and touch no memory); an odd last batch runs on its own.
+    constexpr int LB = D * NBW * TW;                  // loads per batch
+    if (nbatch <= 1) {
+      if (nbatch == 1) {
+        load_batch(0, ta);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(LB));
+      } else {
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+      }
+      asm volatile("s_barrier" ::: "memory");
+      if (nbatch == 1) compute_batch(0, ta);
+    } else if (nbatch == 2) {
+      load_batch(0, ta);
+      load_batch(1, tb);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * LB));
+      asm volatile("s_barrier" ::: "memory");
+      compute_batch(0, ta);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_batch(1, tb);
+    } else {
+      load_batch(0, ta);
+      load_batch(1, tb);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * LB));
+      asm volatile("s_barrier" ::: "memory");
       int b = 0;
       for (; b + 1 < nbatch; b += 2) {
-        compute_batch(b, ta, sa);
+        compute_batch(b, ta);
         __builtin_amdgcn_sched_barrier(0);
-        load_batch(b + 2, ta, sa);
+        load_batch(b + 2, ta);
         __builtin_amdgcn_sched_barrier(0);
-        compute_batch(b + 1, tb, sb);
+        compute_batch(b + 1, tb);
         __builtin_amdgcn_sched_barrier(0);
-        load_batch(b + 3, tb, sb);
+        load_batch(b + 3, tb);
         __builtin_amdgcn_sched_barrier(0);
       }
-      if (b < nbatch) compute_batch(b, ta, sa);
+      if (b < nbatch) compute_batch(b, ta);
     }
   }
 
@@ -443,11 +478,10 @@ bool shape_supported(int nbw, int wn, int wk) {
   return false;
 }
 
-// LDS bytes per staged group: x fragments, rows padded to 16 unless M == 1.
+// LDS bytes per staged group: x fragments (rows padded to 16 unless M == 1)
+// and the 16 scales of each of the workgroup's column blocks.
 int64_t lds_per_group(int wn, int nbw, int mr) {
-  (void)wn;
-  (void)nbw;
-  return mr == 1 ? 256 : 4096;
+  return (mr == 1 ? 256 : 4096) + (int64_t)wn * nbw * 32;
 }
 
 }  // namespace
@@ -470,13 +504,14 @@ bool make_small_plan(int bits, int64_t M, int64_t K, int64_t N, int nbw, int wk,
   const bool own = (nbw == 0 && wk == 0 && splits == 0);
   if (own) {
     // The library's own plan, from sweeps of the decode and verification
-    // shapes on MI355X: one column block per wavefront and four wavefronts
-    // splitting K for one row; for 2-16 rows, wide N shares each staged x
-    // group between eight column blocks (two per wavefront), long K splits
-    // across three workgroups with two K-wavefronts each, and the rest use
-    // four K-wavefronts per column block.
+    // shapes on MI355X: four wavefronts splitting K for one row, each with
+    // two column blocks when N is wide (the offset chain and the x reads
+    // serve both) and one otherwise; for 2-16 rows, wide N shares each
+    // staged x group between eight column blocks (two per wavefront), long K
+    // splits across three workgroups with two K-wavefronts each, and the
+    // rest use four K-wavefronts per column block.
     if (M == 1) {
-      nbw = 1; wk = 4;
+      nbw = NB >= 1024 ? 2 : 1; wk = 4;
     } else if (NB >= 1024) {
       nbw = 2; wk = 1; splits = 1;
     } else if (G >= 40) {
