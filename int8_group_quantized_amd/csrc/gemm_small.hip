@@ -96,10 +96,12 @@ struct Tile {
 // Groups per batch: two batches of D x NBW tiles stay in registers, and a
 // batch's tiles of one column block sit within the 4 KiB immediate-offset
 // reach of a load instruction.
-template <int BITS, int NBW>
+template <int BITS, int NBW, int MR>
 struct Batch {
-  static constexpr int D = (BITS == 4) ? (NBW == 1 ? 4 : (NBW == 2 ? 2 : 1))
-                                       : (NBW == 1 ? 2 : 1);
+  // Two column blocks at M = 1 (five groups per wavefront in the decode
+  // plans) take batches of three so that two batches cover them exactly.
+  static constexpr int D = (BITS == 4) ? (NBW == 1 ? 4 : (NBW == 2 ? (MR == 1 ? 3 : 2) : 1))
+                                       : (NBW == 4 ? 1 : 2);
 };
 
 template <int BITS, bool SBF, bool XH, bool GR, int MR, int NBW, int WN, int WK>
@@ -110,7 +112,7 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_small_kernel(
   constexpr int NW = WN * WK;
   constexpr int TB = Tile<BITS>::bytes;
   constexpr int TW = Tile<BITS>::words;
-  constexpr int D = Batch<BITS, NBW>::D;
+  constexpr int D = Batch<BITS, NBW, MR>::D;
   constexpr int XG = (MR == 1) ? 16 : 256;   // LDS 16-byte words of x per group
   constexpr int CBW = WN * NBW;               // column blocks of the workgroup
   using A = Act<XH>;
