@@ -62,7 +62,8 @@ def test_small_shapes_plans(bits, M, K, N):
 
 
 @pytest.mark.parametrize("bits", [4, 8])
-@pytest.mark.parametrize("M,K,N", [(17, 128, 16), (129, 896, 592), (300, 384, 272)])
+@pytest.mark.parametrize("M,K,N", [(17, 128, 16), (129, 896, 592), (300, 384, 272),
+                                   (8190, 256, 2080)])
 def test_prefill_shapes(bits, M, K, N):
     x, c, s = _inputs(bits, M, K, N, 7 * M + N + 1)
     _close(_run(bits, x, c, s, N), _ref(bits, x, c, s), "prefill M=%d" % M)

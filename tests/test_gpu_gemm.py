@@ -85,9 +85,12 @@ def test_multi_row_blocks(bits, M):
 
 @pytest.mark.parametrize("bits", [4, 8])
 @pytest.mark.parametrize("M,K,N", [(17, 128, 16), (129, 896, 592), (256, 1280, 2048),
-                                   (300, 384, 272), (1000, 256, 4096)])
+                                   (300, 384, 272), (1000, 256, 4096),
+                                   (8190, 256, 2080), (4097, 384, 4112)])
 def test_prefill_shapes(bits, M, K, N):
-    """Prefill kernel: ragged 128 x 128 tiles in M and N, one-group K."""
+    """Prefill kernel: ragged tiles in M and N, one-group K; the last two
+    shapes have enough 128 x 256 tiles for the large-tile plan (ragged in
+    both M and N there too)."""
     x, c, s = _inputs(bits, M, K, N, 7 * M + N)
     ref = gemm.gemm_ref(x, c, s, SDT[bits])
     got = _run(bits, x, c, s, N)
