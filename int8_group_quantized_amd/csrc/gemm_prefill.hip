@@ -24,9 +24,9 @@
 //     matrix core as sum x * q, and one fma per element applies the fp32
 //     scale into the fp32 running sum (exact products, fp32 sums).
 // Tiles are mapped so that each XCD (workgroups are dealt to the eight XCDs
-// round-robin) walks a contiguous run of tiles with the column tile fastest:
-// the 64-row x slice it is working on stays in that XCD's L2 while the
-// packed weight streams past.
+// round-robin) walks its own rows of tiles in panels of eight column tiles:
+// the x slices and weight tiles of the workgroups resident on an XCD at one
+// time stay in that XCD's L2.
 #include "qg_device.h"
 #include "qg_internal.h"
 
@@ -35,6 +35,7 @@ namespace {
 
 constexpr int kBM = 64;                      // rows per workgroup tile
 constexpr int kXcds = 8;
+constexpr int kPanel = 8;                    // column tiles per panel of the tile walk
 constexpr int kXBytes = kBM * kGroup * 2;    // one group of x for the tile: 16 KiB
 
 // One ring stage: x [16 blocks of 1 KiB], the 4 WN weight tiles, and per
@@ -123,12 +124,33 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(2))) vo
   const int NB = N >> 4;
 
   // XCD-aware tile order: workgroup b runs on XCD b % 8; give each XCD a
-  // contiguous range of tiles (identity on the ragged tail).
+  // contiguous range of tiles (identity on the ragged tail). When that range
+  // is whole tile rows, walk it in panels of kPanel column tiles, so the
+  // workgroups resident on one XCD at a time (~8 rows x 8 columns of tiles)
+  // share both their x slices and their weight tiles in that XCD's L2
+  // (measured +4% at 8192 x 2560 x 19456).
   int t = blockIdx.x;
   const int t8 = tiles / kXcds * kXcds;
-  if (t < t8) t = (t % kXcds) * (t8 / kXcds) + t / kXcds;
-  const int tm = t / tiles_n;
-  const int tn = t - tm * tiles_n;
+  const int per = t8 / kXcds;
+  int tm, tn;
+  if (t < t8 && per % tiles_n == 0) {
+    const int xcd = t % kXcds, i = t / kXcds;
+    const int rows_x = per / tiles_n;
+    const int full = tiles_n / kPanel;
+    if (i < full * kPanel * rows_x) {
+      const int pn = i / (rows_x * kPanel), j = i - pn * rows_x * kPanel;
+      tm = xcd * rows_x + j / kPanel;
+      tn = pn * kPanel + j % kPanel;
+    } else {   // the last, narrower panel
+      const int j = i - full * kPanel * rows_x, wt = tiles_n - full * kPanel;
+      tm = xcd * rows_x + j / wt;
+      tn = full * kPanel + j % wt;
+    }
+  } else {
+    if (t < t8) t = (t % kXcds) * per + t / kXcds;
+    tm = t / tiles_n;
+    tn = t - tm * tiles_n;
+  }
   const int m0 = tm * kBM;
   const int cb0 = tn * 4 * WN;
 
