@@ -411,22 +411,51 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_small_kernel(
   __syncthreads();
   if (s_last == 0u) return;
   if (wk == 0) {
+    // Sum the partials in split order. The loads of four splits for all of
+    // the lane's outputs are issued before any is added, so the merge costs
+    // one memory round trip per four splits instead of one per load.
+    constexpr int U = 4;
+    const int64_t sstride = (int64_t)M * ga.n_total;
+    const float* pp[NBW][4];
+    bool ok[NBW][4];
+    float sum[NBW][4];
 #pragma unroll
     for (int c = 0; c < NBW; ++c) {
-      if (c < nvalid) {
-        const int n = (cb0 + c) * 16 + l16;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * lq + e;
-          if (r < mrows) {
-            float sum = 0.0f;
-            for (int sp = 0; sp < splits; ++sp)
-              sum += load_coherent(
-                  &partials[((int64_t)sp * M + row0 + r) * ga.n_total + colp + n]);
-            out[(int64_t)(row0 + r) * N + n] = A::out(sum);
-          }
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * lq + e;
+        ok[c][e] = c < nvalid && r < mrows;
+        pp[c][e] = partials + (int64_t)(row0 + (ok[c][e] ? r : 0)) * ga.n_total + colp +
+                   (ok[c][e] ? (cb0 + c) * 16 + l16 : 0);
+        sum[c][e] = 0.0f;
+      }
+    }
+    for (int sp0 = 0; sp0 < splits; sp0 += U) {
+      float v[U][NBW][4];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const bool in = sp0 + u < splits;
+#pragma unroll
+        for (int c = 0; c < NBW; ++c) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            v[u][c][e] = (in && ok[c][e]) ? load_coherent(pp[c][e] + (sp0 + u) * sstride) : 0.0f;
         }
       }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+#pragma unroll
+        for (int c = 0; c < NBW; ++c) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sum[c][e] += v[u][c][e];
+        }
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < NBW; ++c) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (ok[c][e]) out[(int64_t)(row0 + 4 * lq + e) * N + (cb0 + c) * 16 + l16] = A::out(sum[c][e]);
     }
   }
   if (tid == 0)   // ready for the next call on this workspace
@@ -454,11 +483,13 @@ template <int BITS, bool SBF, bool XH, int MR>
 hipError_t launch_shape(const SmallPlan& p, const void* x, const GroupArgs& g, int64_t M,
                         int64_t K, void* ws, hipStream_t st) {
   if (g.count > 1) {
-    // Groups always take the library's own plan, which uses these shapes.
+    // Groups always take the library's own plan, which uses these shapes
+    // (M = 1: one or two column blocks per wavefront, four K-wavefronts;
+    // 2-16 rows: wide, long-K and the rest).
 #define QG_G(NBW, WN, WK)                                                                    \
     if (p.nbw == NBW && p.wn == WN && p.wk == WK)                                            \
       return launch_variant<BITS, SBF, XH, true, MR, NBW, WN, WK>(p, x, g, M, K, ws, st);
-    QG_G(1, 1, 4) QG_G(2, 4, 1) QG_G(1, 2, 2)
+    QG_G(1, 1, 4) QG_G(2, 1, 4) QG_G(2, 4, 1) QG_G(1, 4, 1)
 #undef QG_G
     return hipErrorInvalidValue;
   }
@@ -510,14 +541,15 @@ bool make_small_plan(int bits, int64_t M, int64_t K, int64_t N, int nbw, int wk,
     // two column blocks when N is wide (the offset chain and the x reads
     // serve both) and one otherwise; for 2-16 rows, wide N shares each
     // staged x group between eight column blocks (two per wavefront), long K
-    // splits across three workgroups with two K-wavefronts each, and the
-    // rest use four K-wavefronts per column block.
+    // splits across workgroups of four column blocks (about 16 INT4 or 13
+    // INT8 groups each), and the rest use four K-wavefronts per column block.
     if (M == 1) {
       nbw = NB >= 1024 ? 2 : 1; wk = 4;
     } else if (NB >= 1024) {
       nbw = 2; wk = 1; splits = 1;
     } else if (G >= 40) {
-      nbw = 1; wk = 2; splits = (int)((G + 25) / 26);
+      const int per = bits == 4 ? 16 : 13;
+      nbw = 1; wk = 1; splits = (int)((G + per - 1) / per);
     } else {
       nbw = 1; wk = 4;
     }

@@ -42,7 +42,8 @@ def _decode(t, act):
 @pytest.mark.parametrize("act", ["bf16", "f16"])
 @pytest.mark.parametrize("M,K,Ns", [(1, 2560, [1024] * 5), (16, 2560, [1024] * 5),
                                     (3, 896, [592, 16, 272]), (16, 9728, [2560, 512]),
-                                    (7, 384, [48] * 16), (40, 512, [96, 208])])
+                                    (7, 384, [48] * 16), (40, 512, [96, 208]),
+                                    (1, 2560, [8192, 8192, 4096]), (16, 9728, [1024, 1536])])
 def test_items_match_the_oracle(bits, act, M, K, Ns):
     x, items = _group(bits, M, K, Ns, 500 + M + len(Ns), act)
     xd = dev_bf16(x) if act == "bf16" else dev_f16(x)
