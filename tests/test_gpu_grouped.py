@@ -38,12 +38,17 @@ def _decode(t, act):
     return numerics.act_to_f64(host_u16(t), act)
 
 
+# The cases reach every tiling the library's plans give a group: one row with
+# narrow and with wide summed N (one or two column blocks per wavefront),
+# 2-16 rows with wide N, long K (split across workgroups) and the rest, and
+# more than 16 rows (the prefill kernel, one launch per item).
 @pytest.mark.parametrize("bits", [4, 8])
 @pytest.mark.parametrize("act", ["bf16", "f16"])
 @pytest.mark.parametrize("M,K,Ns", [(1, 2560, [1024] * 5), (16, 2560, [1024] * 5),
                                     (3, 896, [592, 16, 272]), (16, 9728, [2560, 512]),
                                     (7, 384, [48] * 16), (40, 512, [96, 208]),
-                                    (1, 2560, [8192, 8192, 4096]), (16, 9728, [1024, 1536])])
+                                    (1, 2560, [8192, 8192, 4096]), (16, 9728, [1024, 1536]),
+                                    (4, 2560, [8192, 8192])])
 def test_items_match_the_oracle(bits, act, M, K, Ns):
     x, items = _group(bits, M, K, Ns, 500 + M + len(Ns), act)
     xd = dev_bf16(x) if act == "bf16" else dev_f16(x)
