@@ -19,7 +19,9 @@ Besides the headline line, the same JSON object carries
   workloads     the other shapes (M=16 verification, W8A16 drafter, M=8192
                 prefill, fp16 activations, Q_s packing, dense dequantization,
                 the fake quantizer, the grouped K+V launch, and the drafter's
-                sliding-window attention), each with its roofline fraction.
+                sliding-window attention), each with its roofline fraction;
+                the prefill rows also carry, as context, the vendor
+                library's dense bf16 GEMM (torch.matmul) at the same shape.
 """
 
 import argparse
@@ -189,6 +191,29 @@ def kernel_average(torch, wt, q, launches=400):
     return ms / (100 * (launches // 100))
 
 
+def dense_bf16_reference(torch, M, K, N, reps=10):
+    """Context for the prefill rows: milliseconds per call of the vendor
+    library's plain dense bf16 GEMM (torch.matmul, contiguous [M,K] x [K,N])
+    at the same shape. It is not this library's path and does the same
+    matrix-core work without the code expansion and group scales."""
+    a = torch.randn(M, K, device="cuda").bfloat16()
+    b = torch.randn(K, N, device="cuda").bfloat16()
+    for _ in range(2):
+        torch.matmul(a, b)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        torch.matmul(a, b)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b
+    torch.cuda.empty_cache()
+    return ms
+
+
 def measure_workload(torch, q, cfg, reps=300, act="bf16"):
     import workloads
     w = workloads.WORKLOADS[cfg]
@@ -208,6 +233,9 @@ def measure_workload(torch, q, cfg, reps=300, act="bf16"):
         if prefill:
             tf = wt.flops / (ms * 1e-3) / 1e12
             row.update(tflops=round(tf, 1), frac_bf16_peak=round(tf / BF16_PEAK_TFLOPS, 4))
+            dense = dense_bf16_reference(torch, w["M"], K, N)
+            row.update(dense_bf16_library_us=round(dense * 1e3, 1),
+                       dense_bf16_library_tflops=round(wt.flops / (dense * 1e-3) / 1e12, 1))
         else:
             gbs = wt.bytes / (ms * 1e-3) / 1e9
             row.update(gbs=round(gbs, 1), frac_hbm_peak=round(gbs / HBM_PEAK_GBS, 4),

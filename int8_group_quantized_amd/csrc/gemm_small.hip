@@ -22,10 +22,9 @@
 //     loads, in the lane order of the matrix-core A operand, with rows >= M
 //     stored as zeros (MR = 16) or read from a zero block (MR = 1), so each
 //     group is four unconditional 16-byte LDS reads at immediate offsets.
-//     The staging loads go out before the weight tiles, so waiting for them
-//     does not wait for the tiles. Scales travel with the tiles (one 2-byte
-//     buffer load per tile and lane), so the cold scale rows are never
-//     waited for before the first multiply;
+//     The scales of the workgroup's column blocks follow in one sweep of
+//     16-byte direct loads. The staging loads go out before the weight
+//     tiles, so waiting for them does not wait for the tiles;
 //   * codes expand in registers to exact bf16 integers (seven ALU ops per
 //     eight INT4 codes, twelve per eight INT8 codes); four 16x16x32 bf16
 //     matrix-core ops give a group's fp32 partial sums for 16 rows x 16
