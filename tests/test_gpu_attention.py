@@ -124,6 +124,18 @@ def test_deterministic_and_workspace_reusable():
         np.testing.assert_array_equal(a, b)
 
 
+def test_most_chunks_one_head_merges():
+    # 256 chunks of 32 keys (the most one (sequence, head) may have): the
+    # last workgroup to arrive merges 256 partial results
+    _parity(1, 16, 4, 1, 8192, [8192], 0, 6900, chunk=32)
+
+
+def test_million_token_cache():
+    # a 2^20-position cache per sequence (offsets past 2^28 elements), the
+    # window at its end and in the middle of a shorter sequence
+    _parity(2, 16, 4, 1, 1 << 20, [1 << 20, 600001], 1024, 7000)
+
+
 def test_empty_batch_is_a_no_op():
     qt = torch.empty((0, 16, 20, D), dtype=torch.bfloat16, device=DEV)
     kt = torch.empty((0, 100, 4, D), dtype=torch.bfloat16, device=DEV)

@@ -147,6 +147,17 @@ def test_dequant_bit_exact(bits, s_dtype, out_dtype, K, N):
 
 
 @pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("K,N", [(1 << 20, 16), (128, 1 << 20)])
+def test_dequant_maximum_extents(bits, K, N):
+    """The largest K and N the boundary accepts (2^20), bit-exact."""
+    c = workloads.codes(K, N, bits, 17 + (K >> 7))
+    s = workloads.scales(K // 128, N, SDT[bits], 18 + (K >> 7))
+    pg = q.prepack(dev_i8(c), bits)
+    got = host_u16(q.dequant(pg, dev_scales(s, SDT[bits]), bits, K, N))
+    assert np.array_equal(got, quant.dequant_bits(c, s, SDT[bits], "bf16"))
+
+
+@pytest.mark.parametrize("bits", [4, 8])
 def test_dequant_full_size(bits):
     """The decode gate/up weight (2560 x 19456) through Q_s and back."""
     K, N = 2560, 19456

@@ -80,6 +80,16 @@ def test_shapes_and_other_scale_dtype(bits, K, N):
 
 
 @pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("K,N", [(1 << 20, 16), (128, 1 << 20)])
+def test_maximum_extents(bits, K, N):
+    """The largest K and N the boundary accepts (2^20), bit-exact."""
+    W = workloads.weights(K, N, 13 + (K >> 7))
+    sb = quant.rtn_scales(W, bits)
+    got = host_u16(q.fake_quant(dev_f32(W), dev_scales(sb, SDT[bits]), bits, dtype=torch.bfloat16))
+    assert np.array_equal(got, quant.fake_quant(W, sb, SDT[bits], bits, "bf16"))
+
+
+@pytest.mark.parametrize("bits", [4, 8])
 def test_equals_pack_then_dequant(bits):
     K, N = 2560, 3584
     W = workloads.weights(K, N, 77)

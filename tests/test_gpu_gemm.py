@@ -99,6 +99,19 @@ def test_prefill_shapes(bits, M, K, N):
 
 
 @pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("M,K,N", [(1, 1 << 20, 16), (16, 1 << 20, 16), (17, 1 << 20, 16),
+                                   (1, 128, 1 << 20), (16, 128, 1 << 20), (17, 128, 1 << 20)])
+def test_maximum_extents(bits, M, K, N):
+    """The largest K and N the boundary accepts (2^20 each): 8,192 groups in
+    one column block (hundreds of K splits at M = 16, a 8,192-group K loop
+    in the prefill kernel) and 65,536 column blocks in one group (the widest
+    grids), on each kernel."""
+    x, c, s = _inputs(bits, M, K, N, 31 + M + (K >> 7))
+    ref = gemm.gemm_ref(x, c, s, SDT[bits])
+    _assert_close(_run(bits, x, c, s, N), ref, "M=%d K=%d N=%d" % (M, K, N))
+
+
+@pytest.mark.parametrize("bits", [4, 8])
 def test_prefill_other_scale_dtype(bits):
     """fp16 and bf16 scales are both accepted (configs use fp16 for INT4,
     bf16 for INT8; the other pairing goes through the same kernels)."""

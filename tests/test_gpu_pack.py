@@ -103,6 +103,24 @@ def test_rtn_crafted(bits):
 
 
 @pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("K,N", [(1 << 20, 16), (128, 1 << 20)])
+def test_maximum_extents(bits, K, N):
+    """The largest K and N the boundary accepts (2^20): 8,192 groups of one
+    column block, and 65,536 column blocks of one group; codes, scales and
+    packed bytes bit-exact, unpack and prepack inverse."""
+    Wd, Wf = _weights_for(K, N, 11 + (K >> 7), "f32")
+    sb = quant.rtn_scales(Wf, bits)
+    codes = quant.q_s(Wf, numerics.scale_bits_to_f64(sb, SDT[bits]), bits)
+    sg = q.rtn_scales(Wd, bits)
+    assert np.array_equal(host_u16(sg), sb)
+    pg = q.pack_to_grid(Wd, sg, bits)
+    assert np.array_equal(host_u8(pg), layout.pack(codes, bits))
+    cg = q.unpack(pg, K, N, bits)
+    assert np.array_equal(host_i8(cg), codes)
+    assert torch.equal(q.prepack(cg, bits), pg)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
 @pytest.mark.parametrize("K,N", [(2560, 19456), (9728, 2560), (2560, 3584)])
 def test_full_size_codes(bits, K, N):
     seed = workloads.seed_for(3 if bits == 4 else 4, [(2560, 19456), (9728, 2560),
