@@ -63,19 +63,26 @@ struct LaneCoords {
   int g;
 };
 
+// Wavefronts walk the tiles group-major (consecutive wavefronts take
+// neighbouring column blocks of one group), so a workgroup's loads of the
+// row-major [K, N] array cover 64 adjacent columns: whole cache lines, each
+// fetched once. Each wavefront still writes its own contiguous packed tile.
 template <int BITS>
 __device__ __forceinline__ bool lane_coords(int K, int N, LaneCoords* c) {
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int G = K / kGroup;
-  const int64_t tiles = (int64_t)(N / kTileCols) * G;
-  const int64_t tile = gid >> 6;
-  if (tile >= tiles) return false;
+  const int64_t NB = N / kTileCols;
+  const int64_t tiles = NB * G;
+  const int64_t t = gid >> 6;
+  if (t >= tiles) return false;
   const int lane = (int)(gid & 63);
-  const int64_t nb = tile / G;
-  c->g = (int)(tile - nb * G);
+  const int64_t g = t / NB;
+  const int64_t nb = t - g * NB;
+  c->g = (int)g;
   c->col = nb * kTileCols + (lane & 15);
-  c->row0 = (int64_t)c->g * kGroup + 8 * (lane >> 4);
-  c->out_u4 = (BITS == 4) ? gid : 2 * gid;
+  c->row0 = g * kGroup + 8 * (lane >> 4);
+  const int64_t lane_u4 = (nb * G + g) * 64 + lane;   // packed order: column block major
+  c->out_u4 = (BITS == 4) ? lane_u4 : 2 * lane_u4;
   return true;
 }
 
