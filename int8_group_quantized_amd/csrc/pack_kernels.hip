@@ -15,7 +15,8 @@
 // Thread mapping for the tile kernels: one thread per (tile, lane), i.e. per
 // 16 packed bytes (INT4) or 32 (INT8). A thread's 32 codes share one column
 // and one group, hence one scale. Packed stores are 16-byte vector stores,
-// contiguous across the wavefront (one 1 KiB or 2 KiB tile per wave).
+// contiguous across the wavefront (one 1 KiB or 2 KiB tile per wave);
+// pack_to_grid stages its workgroup's weight block in LDS first.
 #include "qg_device.h"
 #include "qg_internal.h"
 
@@ -117,25 +118,76 @@ __device__ __forceinline__ void store_lane_codes(void* packed, int64_t out_u4, c
   }
 }
 
+// Q_s + packing. A workgroup owns one group (128 rows) of four column
+// blocks (64 columns): it first stages that block of W in LDS as fp32 with
+// 16-byte loads (whole cache lines, a quarter of the load instructions of
+// per-element loads), then each wavefront packs one column block, a lane
+// reading its 32 codes down one column. LDS rows are padded to 66 words so
+// the four row quads of a lane group read 16 banks apart.
+constexpr int kPackRowW = 66;
+
 template <int BITS, bool W_BF16, bool S_BF16>
 __global__ __launch_bounds__(256) void pack_to_grid_kernel(const void* __restrict__ W,
                                                            const uint16_t* __restrict__ scales,
                                                            void* __restrict__ packed, int K, int N) {
-  LaneCoords c;
-  if (!lane_coords<BITS>(K, N, &c)) return;
-  const float s = scale_to_f32(scales[(int64_t)c.g * N + c.col], S_BF16);
+  __shared__ float tw[kGroup * kPackRowW];
+  const int G = K / kGroup;
+  const int NB = N / kTileCols;
+  const int g = blockIdx.y;
+  const int col0 = blockIdx.x * 64;
+  const int ncols = min(64, N - col0);            // a multiple of 16
+  const int tid = threadIdx.x;
+  const int64_t row_base = (int64_t)g * kGroup;
+  if constexpr (W_BF16) {
+    // 8 lanes per 128-byte row, 32 rows per pass.
+    const int ch = tid & 7;
+    if (8 * ch < ncols) {
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int r = (tid >> 3) + 32 * p;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(
+            static_cast<const uint16_t*>(W) + (row_base + r) * N + col0 + 8 * ch);
+        float* d = tw + r * kPackRowW + 8 * ch;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          *reinterpret_cast<float2*>(d + 2 * e) =
+              float2{bf16_bits_to_f32(v[e] & 0xFFFFu), bf16_bits_to_f32(v[e] >> 16)};
+        }
+      }
+    }
+  } else {
+    // 16 lanes per 256-byte row, 16 rows per pass.
+    const int ch = tid & 15;
+    if (4 * ch < ncols) {
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {
+        const int r = (tid >> 4) + 16 * p;
+        const float4 v = *reinterpret_cast<const float4*>(
+            static_cast<const float*>(W) + (row_base + r) * N + col0 + 4 * ch);
+        float* d = tw + r * kPackRowW + 4 * ch;
+        *reinterpret_cast<float2*>(d) = float2{v.x, v.y};
+        *reinterpret_cast<float2*>(d + 2) = float2{v.z, v.w};
+      }
+    }
+  }
+  __syncthreads();
+  const int wave = tid >> 6, lane = tid & 63;
+  const int nb = blockIdx.x * 4 + wave;
+  if (nb >= NB) return;
+  const int cw = 16 * wave + (lane & 15);           // column within the block of 64
+  const float s = scale_to_f32(scales[(int64_t)g * N + col0 + cw], S_BF16);
   const float lo = (BITS == 4) ? -8.0f : -127.0f;
   const float hi = (BITS == 4) ? 7.0f : 127.0f;
+  const int r0 = 8 * (lane >> 4);
   int q[32];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int64_t k = c.row0 + 32 * j + i;
-      q[8 * j + i] = quantize_to_grid(load_weight<W_BF16>(W, k * N + c.col), s, lo, hi);
-    }
+    for (int i = 0; i < 8; ++i)
+      q[8 * j + i] = quantize_to_grid(tw[(r0 + 32 * j + i) * kPackRowW + cw], s, lo, hi);
   }
-  store_lane_codes<BITS>(packed, c.out_u4, q);
+  const int64_t lane_u4 = ((int64_t)nb * G + g) * 64 + lane;
+  store_lane_codes<BITS>(packed, (BITS == 4) ? lane_u4 : 2 * lane_u4, q);
 }
 
 template <int BITS>
@@ -333,7 +385,7 @@ hipError_t launch_rtn_scales(int bits, const void* W, bool w_bf16, int64_t K, in
 
 hipError_t launch_pack_to_grid(int bits, const void* W, bool w_bf16, const void* scales,
                                bool s_bf16, int64_t K, int64_t N, void* packed, hipStream_t st) {
-  const dim3 grid = tile_grid(K, N);
+  const dim3 grid((unsigned)((N / kTileCols + 3) / 4), (unsigned)(K / kGroup));
   const auto* s = static_cast<const uint16_t*>(scales);
   const int k = (int)K, n = (int)N;
 #define QG_PACK(B, WB, SB) pack_to_grid_kernel<B, WB, SB><<<grid, 256, 0, st>>>(W, s, packed, k, n)
