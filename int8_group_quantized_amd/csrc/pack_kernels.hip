@@ -55,38 +55,8 @@ __global__ __launch_bounds__(256) void rtn_scales_kernel(const void* __restrict_
   scales[(int64_t)g * N + n] = (BITS == 4) ? f32_to_f16_bits(s) : f32_to_bf16_bits(s);
 }
 
-// Gather the 32 logical values of one (tile, lane) in element order:
-// v[j*8 + i] is k = 128g + 32j + 8*(lane/16) + i, column 16*nb + lane%16.
-struct LaneCoords {
-  int64_t col;      // n
-  int64_t row0;     // k of element (j=0, i=0)
-  int64_t out_u4;   // index of the lane's first 16-byte word in the packed array
-  int g;
-};
-
-// Wavefronts walk the tiles group-major (consecutive wavefronts take
-// neighbouring column blocks of one group), so a workgroup's loads of the
-// row-major [K, N] array cover 64 adjacent columns: whole cache lines, each
-// fetched once. Each wavefront still writes its own contiguous packed tile.
-template <int BITS>
-__device__ __forceinline__ bool lane_coords(int K, int N, LaneCoords* c) {
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int G = K / kGroup;
-  const int64_t NB = N / kTileCols;
-  const int64_t tiles = NB * G;
-  const int64_t t = gid >> 6;
-  if (t >= tiles) return false;
-  const int lane = (int)(gid & 63);
-  const int64_t g = t / NB;
-  const int64_t nb = t - g * NB;
-  c->g = (int)g;
-  c->col = nb * kTileCols + (lane & 15);
-  c->row0 = g * kGroup + 8 * (lane >> 4);
-  const int64_t lane_u4 = (nb * G + g) * 64 + lane;   // packed order: column block major
-  c->out_u4 = (BITS == 4) ? lane_u4 : 2 * lane_u4;
-  return true;
-}
-
+// The 32 logical values of one (tile, lane), in element order: q[j*8 + i] is
+// k = 128g + 32j + 8*(lane/16) + i, column 16*nb + lane%16.
 template <int BITS>
 __device__ __forceinline__ void store_lane_codes(void* packed, int64_t out_u4, const int (&q)[32]) {
   u32x4* dst = static_cast<u32x4*>(packed) + out_u4;
@@ -190,47 +160,103 @@ __global__ __launch_bounds__(256) void pack_to_grid_kernel(const void* __restric
   store_lane_codes<BITS>(packed, (BITS == 4) ? lane_u4 : 2 * lane_u4, q);
 }
 
+// prepack / unpack move int8 codes [K, N] (row-major) to and from the
+// packed tiles through LDS, one workgroup per group of 64 columns, so the
+// code array is read or written with 16-byte row accesses (a lane's 32
+// codes run down one column: one byte per row). LDS rows are 68 bytes, so
+// the four row quads of a lane group sit 8 banks apart.
+constexpr int kCodeRowB = 68;
+
 template <int BITS>
 __global__ __launch_bounds__(256) void prepack_kernel(const int8_t* __restrict__ codes,
                                                       void* __restrict__ packed, int K, int N) {
-  LaneCoords c;
-  if (!lane_coords<BITS>(K, N, &c)) return;
+  __shared__ uint32_t tc[kGroup * kCodeRowB / 4];
+  unsigned char* tb = reinterpret_cast<unsigned char*>(tc);
+  const int G = K / kGroup;
+  const int NB = N / kTileCols;
+  const int g = blockIdx.y;
+  const int col0 = blockIdx.x * 64;
+  const int ncols = min(64, N - col0);            // a multiple of 16
+  const int tid = threadIdx.x;
+  const int ch = tid & 3;
+  if (16 * ch < ncols) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int r = (tid >> 2) + 64 * p;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(codes + ((int64_t)g * kGroup + r) * N + col0 +
+                                                      16 * ch);
+      uint32_t* d = tc + (r * kCodeRowB + 16 * ch) / 4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) d[e] = v[e];
+    }
+  }
+  __syncthreads();
+  const int wave = tid >> 6, lane = tid & 63;
+  const int nb = blockIdx.x * 4 + wave;
+  if (nb >= NB) return;
+  const int cw = 16 * wave + (lane & 15);
+  const int r0 = 8 * (lane >> 4);
   int q[32];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) q[8 * j + i] = codes[(c.row0 + 32 * j + i) * N + c.col];
+    for (int i = 0; i < 8; ++i) q[8 * j + i] = (int8_t)tb[(r0 + 32 * j + i) * kCodeRowB + cw];
   }
-  store_lane_codes<BITS>(packed, c.out_u4, q);
+  const int64_t lane_u4 = ((int64_t)nb * G + g) * 64 + lane;
+  store_lane_codes<BITS>(packed, (BITS == 4) ? lane_u4 : 2 * lane_u4, q);
 }
 
 template <int BITS>
 __global__ __launch_bounds__(256) void unpack_kernel(const void* __restrict__ packed,
                                                      int8_t* __restrict__ codes, int K, int N) {
-  LaneCoords c;
-  if (!lane_coords<BITS>(K, N, &c)) return;
-  const u32x4* src = static_cast<const u32x4*>(packed) + c.out_u4;
-  int q[32];
-  if constexpr (BITS == 4) {
-    const u32x4 w = src[0];
+  __shared__ uint32_t tc[kGroup * kCodeRowB / 4];
+  unsigned char* tb = reinterpret_cast<unsigned char*>(tc);
+  const int G = K / kGroup;
+  const int NB = N / kTileCols;
+  const int g = blockIdx.y;
+  const int col0 = blockIdx.x * 64;
+  const int ncols = min(64, N - col0);
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int nb = blockIdx.x * 4 + wave;
+  if (nb < NB) {
+    const int64_t lane_u4 = ((int64_t)nb * G + g) * 64 + lane;
+    const u32x4* src = static_cast<const u32x4*>(packed) + ((BITS == 4) ? lane_u4 : 2 * lane_u4);
+    int q[32];
+    if constexpr (BITS == 4) {
+      const u32x4 w = src[0];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < 4; ++j) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) q[8 * j + i] = (int)((w[j] >> (4 * nibble_of(i))) & 15u) - 8;
+        for (int i = 0; i < 8; ++i) q[8 * j + i] = (int)((w[j] >> (4 * nibble_of(i))) & 15u) - 8;
+      }
+    } else {
+      const u32x4 a = src[0], b = src[1];
+      const uint32_t words[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[8 * j + i] = (int8_t)(words[2 * j + (i >> 2)] >> (8 * (i & 3)));
+      }
     }
-  } else {
-    const u32x4 a = src[0], b = src[1];
-    const uint32_t words[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    const int cw = 16 * wave + (lane & 15);
+    const int r0 = 8 * (lane >> 4);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) q[8 * j + i] = (int8_t)(words[2 * j + (i >> 2)] >> (8 * (i & 3)));
+      for (int i = 0; i < 8; ++i) tb[(r0 + 32 * j + i) * kCodeRowB + cw] = (unsigned char)q[8 * j + i];
     }
   }
+  __syncthreads();
+  const int ch = tid & 3;
+  if (16 * ch < ncols) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) codes[(c.row0 + 32 * j + i) * N + c.col] = (int8_t)q[8 * j + i];
+    for (int p = 0; p < 2; ++p) {
+      const int r = (tid >> 2) + 64 * p;
+      const uint32_t* d = tc + (r * kCodeRowB + 16 * ch) / 4;
+      *reinterpret_cast<u32x4*>(codes + ((int64_t)g * kGroup + r) * N + col0 + 16 * ch) =
+          u32x4{d[0], d[1], d[2], d[3]};
+    }
   }
 }
 
@@ -362,10 +388,6 @@ __global__ __launch_bounds__(256) void fake_quant_kernel(const void* __restrict_
   }
 }
 
-dim3 tile_grid(int64_t K, int64_t N) {
-  const int64_t lanes = (K / kGroup) * (N / kTileCols) * 64;
-  return dim3((unsigned)((lanes + 255) / 256));
-}
 
 }  // namespace
 
@@ -402,7 +424,7 @@ hipError_t launch_pack_to_grid(int bits, const void* W, bool w_bf16, const void*
 
 hipError_t launch_prepack(int bits, const int8_t* codes, int64_t K, int64_t N, void* packed,
                           hipStream_t st) {
-  const dim3 grid = tile_grid(K, N);
+  const dim3 grid((unsigned)((N / kTileCols + 3) / 4), (unsigned)(K / kGroup));
   if (bits == 4) prepack_kernel<4><<<grid, 256, 0, st>>>(codes, packed, (int)K, (int)N);
   else           prepack_kernel<8><<<grid, 256, 0, st>>>(codes, packed, (int)K, (int)N);
   return hipGetLastError();
@@ -410,7 +432,7 @@ hipError_t launch_prepack(int bits, const int8_t* codes, int64_t K, int64_t N, v
 
 hipError_t launch_unpack(int bits, const void* packed, int64_t K, int64_t N, int8_t* codes,
                          hipStream_t st) {
-  const dim3 grid = tile_grid(K, N);
+  const dim3 grid((unsigned)((N / kTileCols + 3) / 4), (unsigned)(K / kGroup));
   if (bits == 4) unpack_kernel<4><<<grid, 256, 0, st>>>(packed, codes, (int)K, (int)N);
   else           unpack_kernel<8><<<grid, 256, 0, st>>>(packed, codes, (int)K, (int)N);
   return hipGetLastError();
