@@ -21,8 +21,11 @@
 //                 the result holds, per lane, one query (lane % 16) and four
 //                 keys 4(lane / 16) + e of a 16-key block;
 //   O^T = V^T P^T B = P^T straight from those registers (two 16-key blocks
-//                 give the 8 keys a lane supplies), A = V^T gathered from a
-//                 per-wavefront LDS copy of the step's 32 value rows.
+//                 give the 8 keys a lane supplies), A = V^T read from a
+//                 per-wavefront LDS copy of the step's 32 value rows with
+//                 gfx950's transposing LDS read: in each group of 16 lanes,
+//                 lane s names four consecutive 16-bit values (row s) and
+//                 lane t receives element t % 4 of rows t / 4 + 4e, e < 4.
 // P is split into a bf16 high part and the bf16 rounding of the remainder,
 // so P V is accumulated with ~2^-18 relative error in P (two instructions
 // per block) instead of bf16's 2^-9.
@@ -42,8 +45,8 @@ namespace {
 
 constexpr int kD = 128;                        // head dimension
 constexpr int kRowBytes = kD * 2;
-constexpr int kVGroupBytes = 4 * kRowBytes + 32;   // four value rows + pad
-constexpr int kVStageBytes = 8 * kVGroupBytes;     // one step: 32 value rows
+constexpr int kVRowBytes = kRowBytes + 32;        // a value row + pad (rows 8 banks apart)
+constexpr int kVStageBytes = 32 * kVRowBytes;      // one step: 32 value rows
 constexpr int kWaves = 4;
 constexpr int kWavesLds = kWaves * kVStageBytes;
 constexpr int kOFloats = 16 * kD;                  // one chunk's O[16][128]
@@ -144,7 +147,7 @@ __global__ __launch_bounds__(256, 2) void swa_attention_kernel(
   auto stage_v = [&]() {
 #pragma unroll
     for (int r = 0; r < 8; ++r)
-      *reinterpret_cast<u32x4*>(vst + r * kVGroupBytes + g * kRowBytes + 16 * tok) = vn[r];
+      *reinterpret_cast<u32x4*>(vst + (4 * r + g) * kVRowBytes + 16 * tok) = vn[r];
   };
 
   float m_run = -INFINITY, l_run = 0.0f;
@@ -158,8 +161,14 @@ __global__ __launch_bounds__(256, 2) void swa_attention_kernel(
     load_v(k0 + 32 * s);
     stage_v();
   }
-  // Gather base for V^T: key 4g + i (i < 4) or 16 + 4g + (i - 4), dim 16 db + tok.
-  const uint16_t* vg = reinterpret_cast<const uint16_t*>(vst + g * kVGroupBytes) + tok;
+  // V^T operand of lane (tok, g): dim 16 db + tok of keys 4g .. 4g+3 and
+  // 16 + 4g .. +3. Through the transposing read, lane s of the group names
+  // key k0 + s / 4, dims 16 db + 4 (s % 4) .. +3 (8 bytes), and receives
+  // keys k0 .. k0+3 of dim 16 db + s.
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4s* lds_v4s;
+  const char* vt0 = vst + (4 * g + (tok >> 2)) * kVRowBytes + 8 * (tok & 3);
+  const char* vt1 = vt0 + 16 * kVRowBytes;
   for (; s < nsteps; s += kWaves) {
     const int key0 = k0 + 32 * s;
     const bool more = s + kWaves < nsteps;
@@ -209,14 +218,10 @@ __global__ __launch_bounds__(256, 2) void swa_attention_kernel(
     }
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
-      u32x4 av;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const int i0 = 2 * w, i1 = 2 * w + 1;
-        const uint32_t a0 = vg[((i0 >> 2) * 4 * kVGroupBytes + (i0 & 3) * kRowBytes) / 2 + 16 * db];
-        const uint32_t a1 = vg[((i1 >> 2) * 4 * kVGroupBytes + (i1 & 3) * kRowBytes) / 2 + 16 * db];
-        av[w] = a0 | (a1 << 16);
-      }
+      const v4s r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(vt0 + 32 * db));
+      const v4s r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(vt1 + 32 * db));
+      const u32x2 w0 = __builtin_bit_cast(u32x2, r0), w1 = __builtin_bit_cast(u32x2, r1);
+      const u32x4 av = {w0[0], w0[1], w1[0], w1[1]};
       f32x4 od = o[db] * alpha;
       od = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
                                                    __builtin_bit_cast(bf16x8, phi), od, 0, 0, 0);
