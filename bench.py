@@ -170,6 +170,18 @@ def time_graphs(torch, graphs, reps=1):
     return e0.elapsed_time(e1)
 
 
+def time_steady(torch, g, reps, warm_ms=20.0):
+    """Milliseconds for `reps` replays of graph g, timed after untimed replays
+    that keep the GPU busy for about warm_ms: the clocks settle over the
+    first milliseconds of work, and a short timed region taken cold reads up
+    to ~15% slow at the small-M shapes."""
+    first = time_graphs(torch, [g])
+    extra = min(1000, int(warm_ms / max(first, 1e-3)))
+    if extra:
+        time_graphs(torch, [g], reps=extra)
+    return time_graphs(torch, [g], reps=reps)
+
+
 def graphs_for_steps(torch, step, steps):
     full, rem = divmod(steps, GRAPH_CHUNK)
     gs = []
@@ -185,9 +197,7 @@ def kernel_average(torch, wt, q, launches=400):
     """Average duration of one GEMM launch: a graph of back-to-back launches
     on rotating weight copies, timed with events."""
     g = capture(torch, lambda i: wt.call(q, i), 100)
-    for _ in range(2):
-        g.replay()
-    ms = time_graphs(torch, [g], reps=launches // 100)
+    ms = time_steady(torch, g, reps=launches // 100)
     return ms / (100 * (launches // 100))
 
 
@@ -198,7 +208,7 @@ def dense_bf16_reference(torch, M, K, N, reps=10):
     matrix-core work without the code expansion and group scales."""
     a = torch.randn(M, K, device="cuda").bfloat16()
     b = torch.randn(K, N, device="cuda").bfloat16()
-    for _ in range(2):
+    for _ in range(25):                  # ~20 ms of warm-up, as for the library's rows
         torch.matmul(a, b)
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
@@ -214,7 +224,7 @@ def dense_bf16_reference(torch, M, K, N, reps=10):
     return ms
 
 
-def measure_workload(torch, q, cfg, reps=300, act="bf16"):
+def measure_workload(torch, q, cfg, reps=1000, act="bf16"):
     import workloads
     w = workloads.WORKLOADS[cfg]
     rows = []
@@ -225,9 +235,8 @@ def measure_workload(torch, q, cfg, reps=300, act="bf16"):
         wt.W = None
         n = 4 if prefill else 100
         g = capture(torch, lambda i: wt.call(q, i), n)
-        g.replay()
         r = max(1, (20 if prefill else reps) // n)
-        ms = time_graphs(torch, [g], reps=r) / (n * r)
+        ms = time_steady(torch, g, reps=r) / (n * r)
         row = {"shape": workloads.SHAPE_NAMES.get((K, N), "%dx%d" % (K, N)), "M": w["M"],
                "K": K, "N": N, "bits": w["bits"], "us_per_call": round(ms * 1e3, 3)}
         if prefill:
@@ -280,8 +289,7 @@ def measure_dequant(torch, q):
     dense = torch.empty((K, N), dtype=torch.bfloat16, device="cuda")
     g = capture(torch, lambda i: q.dequant(wt.packed[i % wt.copies], wt.scales[i % wt.copies], 4,
                                            K, N, out=dense), 20)
-    g.replay()
-    ms = time_graphs(torch, [g], reps=5) / 100
+    ms = time_steady(torch, g, reps=5) / 100
     nbytes = K * N // 2 + (K // 128) * N * 2 + K * N * 2
     gbs = nbytes / (ms * 1e-3) / 1e9
     wt.free()
@@ -300,8 +308,7 @@ def measure_fake_quant(torch, q):
     s = q.rtn_scales(W, 4)
     out = torch.empty((K, N), dtype=torch.bfloat16, device="cuda")
     g = capture(torch, lambda i: q.fake_quant(W, s, 4, out=out), 20)
-    g.replay()
-    ms = time_graphs(torch, [g], reps=5) / 100
+    ms = time_steady(torch, g, reps=5) / 100
     nbytes = K * N * 4 + (K // 128) * N * 2 + K * N * 2
     gbs = nbytes / (ms * 1e-3) / 1e9
     del g, W, out
@@ -339,10 +346,8 @@ def measure_grouped(torch, q, bits):
     g1 = capture(torch, lambda i: q.qgemm_grouped(x, sets[i % copies], bits, outs=outs, ws=ws), 50)
     g2 = capture(torch, lambda i: [q.qgemm(x, p, sc, bits, n, out=o, ws=ws)
                                    for (p, sc, n), o in zip(sets[i % copies], outs)], 50)
-    g1.replay()
-    g2.replay()
-    t1 = time_graphs(torch, [g1], reps=4) / 200
-    t2 = time_graphs(torch, [g2], reps=4) / 200
+    t1 = time_steady(torch, g1, reps=4) / 200
+    t2 = time_steady(torch, g2, reps=4) / 200
     nbytes = per + M * K * 2 + L * M * N * 2
     gbs = nbytes / (t1 * 1e-3) / 1e9
     del g1, g2, sets, base
@@ -377,8 +382,7 @@ def measure_attention(torch, q, window, B=1):
                      dtype=torch.uint8, device="cuda")
     g = capture(torch, lambda i: q.swa_attention(qt, k_all[i % copies], v_all[i % copies], lens,
                                                  window, out=out, ws=ws), 100)
-    g.replay()
-    us = time_graphs(torch, [g], reps=4) / 400 * 1e3
+    us = time_steady(torch, g, reps=4) / 400 * 1e3
     del g, k_all, v_all
     torch.cuda.empty_cache()
     gbs = nbytes / (us * 1e-6) / 1e9
