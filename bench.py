@@ -201,6 +201,23 @@ def kernel_average(torch, wt, q, launches=400):
     return ms / (100 * (launches // 100))
 
 
+def read_stream_ceiling(torch, q, bufs, widths=(1024, 2048, 4096, 8192, 16384)):
+    """The library's read-stream probe (a measurement aid: plain 16-byte
+    loads, nothing computed) over the rotating buffers bufs, one whole buffer
+    per launch, in HIP-graph replays like the GEMV; the fastest of a few
+    launch widths. Returns (us per launch, bytes per launch, workgroups)."""
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    nbytes = bufs[0].numel() * bufs[0].element_size()
+    best = None
+    for wgs in widths:
+        g = capture(torch, lambda i: q.read_stream(bufs[i % len(bufs)], wgs, sink), 100)
+        us = time_steady(torch, g, reps=4) / 400 * 1e3
+        del g
+        if best is None or us < best[0]:
+            best = (us, nbytes, wgs)
+    return best
+
+
 def dense_bf16_reference(torch, M, K, N, reps=10):
     """Context for the prefill rows: milliseconds per call of the vendor
     library's plain dense bf16 GEMM (torch.matmul, contiguous [M,K] x [K,N])
@@ -459,10 +476,26 @@ def main():
 
     k_ms = kernel_average(torch, up, q)
     k_gbs = up.bytes / (k_ms * 1e-3) / 1e9
+    # Context: what one launch streaming the same weight copies reaches on this
+    # GPU (the packed codes, 24.9 MB per launch), and the rate of 256 MiB reads.
+    c_us, c_bytes, c_wgs = read_stream_ceiling(torch, q, up.packed)
+    big = [torch.empty(1 << 28, dtype=torch.uint8, device="cuda") for _ in range(3)]
+    b_us, b_bytes, b_wgs = read_stream_ceiling(torch, q, big)
+    del big
+    c_gbs, b_gbs = c_bytes / c_us / 1e3, b_bytes / b_us / 1e3
     roofline = {"bound": "hbm", "achieved": round(k_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(k_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                 "kernel": "gemm_small_kernel<4,...> gate/up K=2560 N=19456 M=1",
-                "us_per_launch": round(k_ms * 1e3, 3), "bytes_per_launch": up.bytes}
+                "us_per_launch": round(k_ms * 1e3, 3), "bytes_per_launch": up.bytes,
+                "read_stream_ceiling": {
+                    "probe": "qg_read_stream, 16-byte nontemporal loads, fastest of "
+                             "1024-16384 workgroups",
+                    "bytes_per_launch": c_bytes, "us_per_launch": round(c_us, 3),
+                    "gbs": round(c_gbs, 1), "workgroups": c_wgs,
+                    "frac_of_peak": round(c_gbs / HBM_PEAK_GBS, 4),
+                    "gemv_frac_of_ceiling": round(k_gbs / c_gbs, 4),
+                    "large_read_bytes": b_bytes, "large_read_gbs": round(b_gbs, 1),
+                    "large_read_frac_of_peak": round(b_gbs / HBM_PEAK_GBS, 4)}}
     del graphs
     up.free()
     down.free()

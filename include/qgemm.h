@@ -321,6 +321,24 @@ qg_status qg_swa_attention_chunk(const void* q, const void* k_cache, const void*
                                  int64_t window, float scale, int64_t chunk, void* workspace,
                                  size_t workspace_bytes, void* stream);
 
+/* Read-stream probe: a measurement aid, not a step of the method. Reads
+ * [src, src + bytes) once with 16-byte nontemporal vector loads over
+ * `workgroups` workgroups of 256 threads (grid stride, four loads in flight
+ * per thread)
+ * and discards the data; a launch over a buffer that the 256 MB Infinity
+ * Cache cannot hold measures the rate at which this GPU streams `bytes` from
+ * HBM in one launch, the ceiling the HBM-bound entry points are reported
+ * against beside the 8 TB/s figure.
+ *   src         bytes bytes; bytes a positive multiple of 16, below 2^40
+ *   workgroups  1 .. 65536
+ *   sink        4 bytes, written only when the XOR of the 32-bit words one
+ *               thread reads equals 0x9E3779B9 (the value then stored), so the
+ *               loads cannot be optimised away; otherwise untouched
+ * src and sink follow the pointer rules above (QG_ERR_NULL, QG_ERR_ALIGN);
+ * a bad size or workgroup count is QG_ERR_SHAPE. */
+qg_status qg_read_stream(const void* src, size_t bytes, int workgroups, void* sink,
+                         void* stream);
+
 #ifdef __cplusplus
 }
 #endif

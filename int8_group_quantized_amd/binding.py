@@ -75,6 +75,7 @@ _SIGNATURES = {
     "qg_swa_attention": ([_P, _P, _P, _P, _P] + [_I64] * 7 + [ctypes.c_float, _P, _SZ, _P], _INT),
     "qg_swa_attention_chunk": ([_P, _P, _P, _P, _P] + [_I64] * 7 + [ctypes.c_float, _I64, _P, _SZ,
                                                                      _P], _INT),
+    "qg_read_stream": ([_P, _SZ, _INT, _P, _P], _INT),
 }
 
 
@@ -343,3 +344,16 @@ def swa_attention(q, k_cache, v_cache, seq_lens, window, scale=None, out=None, w
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), _ptr(out), B, T, Hq, Hkv, D, S_max,
         window, scale, chunk, _ptr(ws), ws_bytes, _stream(q)))
     return out
+
+
+READ_PROBE_MARK = 0x9E3779B9
+
+
+def read_stream(buf, workgroups, sink):
+    """Measurement aid: read the bytes of the contiguous GPU tensor buf once
+    (qg_read_stream). sink is a GPU tensor of at least 4 bytes; it receives
+    READ_PROBE_MARK only when one thread's XOR of its words equals it."""
+    _need_cuda(buf, sink)
+    nbytes = buf.numel() * buf.element_size()
+    _check("qg_read_stream", lib().qg_read_stream(_ptr(buf), nbytes, workgroups, _ptr(sink),
+                                                  _stream(buf)))

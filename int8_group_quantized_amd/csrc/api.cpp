@@ -490,4 +490,12 @@ qg_status qg_swa_attention_chunk(const void* q, const void* k_cache, const void*
                        scale, chunk, workspace, workspace_bytes, stream);
 }
 
+qg_status qg_read_stream(const void* src, size_t bytes, int workgroups, void* sink, void* stream) {
+  if (bytes == 0 || bytes % 16 != 0 || bytes >= (size_t(1) << 40)) return QG_ERR_SHAPE;
+  if (workgroups < 1 || workgroups > 65536) return QG_ERR_SHAPE;
+  const qg_status s = check_ptrs({src, sink});
+  if (s != QG_OK) return s;
+  return from_hip(qg::launch_read_stream(src, (int64_t)bytes, workgroups, sink, as_stream(stream)));
+}
+
 }  // extern "C"

@@ -90,6 +90,11 @@ template <int BITS>
 struct Tile {
   static constexpr int bytes = (BITS == 4) ? 1024 : 2048;
   static constexpr int words = bytes / 1024;   // 16-byte words per lane
+  // Cache policy of the tile loads: INT4 tiles, read exactly once, stream
+  // with the nontemporal hint (measured 2-3% faster at M = 1 and 16); the
+  // same hint made the INT8 M = 16 gate/up GEMM 12.9 -> 16.5 µs, so INT8
+  // tiles load with the default policy.
+  static constexpr int aux = (BITS == 4) ? 2 : 0;
 };
 
 // Groups per batch: two batches of D x NBW tiles stay in registers, and a
@@ -193,7 +198,8 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_small_kernel(
 #pragma unroll
           for (int v = 0; v < TW; ++v)
             t[d][c][v] = __builtin_bit_cast(
-                u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, lane_off + d * TB + 16 * v, 0, 0));
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, lane_off + d * TB + 16 * v, 0,
+                                                      Tile<BITS>::aux));
         }
       }
     };

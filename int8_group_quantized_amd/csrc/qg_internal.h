@@ -112,4 +112,11 @@ hipError_t launch_swa_attention(const SwaPlan& p, const void* q, const void* k, 
                                 int64_t Hkv, int64_t S_max, float scale, void* ws,
                                 hipStream_t st);
 
+// Read-stream probe (read_probe.hip): reads bytes (a multiple of 16) at src
+// once over `workgroups` workgroups of 256 threads; stores kReadProbeMark to
+// sink only when a thread's XOR of what it read equals it.
+constexpr uint32_t kReadProbeMark = 0x9E3779B9u;
+hipError_t launch_read_stream(const void* src, int64_t bytes, int workgroups, void* sink,
+                              hipStream_t st);
+
 }  // namespace qg

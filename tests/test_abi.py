@@ -232,3 +232,17 @@ def test_swa_workspace_sizes():
     # a window wider than the cache is no window
     assert L.qg_swa_workspace_bytes(1, 16, 20, 4, 128, 1000, 5000) == \
         L.qg_swa_workspace_bytes(1, 16, 20, 4, 128, 1000, 0)
+
+
+@pytest.mark.parametrize("nbytes,wgs", [(0, 1), (17, 1), (8, 1), (1 << 40, 1), (16, 0), (16, 65537),
+                                        (16, -1)])
+def test_read_stream_bad_sizes(nbytes, wgs):
+    assert q.lib().qg_read_stream(FAKE, nbytes, wgs, FAKE, None) == SHAPE
+
+
+def test_read_stream_bad_pointers():
+    L = q.lib()
+    assert L.qg_read_stream(0, 16, 1, FAKE, None) == NULL
+    assert L.qg_read_stream(FAKE, 16, 1, 0, None) == NULL
+    assert L.qg_read_stream(MIS, 16, 1, FAKE, None) == ALIGN
+    assert L.qg_read_stream(FAKE, 16, 1, MIS, None) == ALIGN
