@@ -280,17 +280,10 @@ def measure_pack(torch, q):
     K, N = 2560, 19456
     W = torch.from_numpy(workloads.weights(K, N, workloads.seed_for(3, 0, 0))).cuda()
     s = q.rtn_scales(W, 4)
-    for _ in range(3):
-        q.pack_to_grid(W, s, 4)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    n = 20
-    for _ in range(n):
-        q.pack_to_grid(W, s, 4)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / n
+    packed = torch.empty(K * N // 2, dtype=torch.uint8, device="cuda")
+    g = capture(torch, lambda i: q.pack_to_grid(W, s, 4, out=packed), 20)
+    ms = time_steady(torch, g, reps=5) / 100
+    del g
     nbytes = K * N * 4 + (K // 128) * N * 2 + K * N // 2
     gbs = nbytes / (ms * 1e-3) / 1e9
     return {"workload": "pack_to_grid_w4 fp32 W", "K": K, "N": N, "us_per_call": round(ms * 1e3, 2),

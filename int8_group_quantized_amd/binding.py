@@ -172,11 +172,15 @@ def rtn_scales(W, bits):
     return s
 
 
-def pack_to_grid(W, scales, bits):
-    """Q_s(W) under the given scales, packed; returns a uint8 tensor."""
-    _need_cuda(W, scales)
+def pack_to_grid(W, scales, bits, out=None):
+    """Q_s(W) under the given scales, packed; returns a uint8 tensor (out, if
+    given: a contiguous GPU tensor of packed_bytes(bits, K, N) bytes)."""
+    _need_cuda(W, scales, out)
     K, N = W.shape
-    out = torch.empty(packed_bytes(bits, K, N), dtype=torch.uint8, device=W.device)
+    if out is None:
+        out = torch.empty(packed_bytes(bits, K, N), dtype=torch.uint8, device=W.device)
+    elif out.numel() * out.element_size() != packed_bytes(bits, K, N):
+        raise ValueError("out must hold packed_bytes(bits, K, N) bytes")
     fn = "qg_pack_to_grid_w%d" % bits
     _check(fn, getattr(lib(), fn)(_ptr(W), _dt(W), _ptr(scales), _dt(scales), K, N, _ptr(out),
                                   _stream(W)))
