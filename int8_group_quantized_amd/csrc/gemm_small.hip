@@ -416,10 +416,14 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_small_kernel(
   __syncthreads();
   if (s_last == 0u) return;
   if (wk == 0) {
-    // Sum the partials in split order. The loads of four splits for all of
-    // the lane's outputs are issued before any is added, so the merge costs
-    // one memory round trip per four splits instead of one per load.
-    constexpr int U = 4;
+    // Sum the partials in split order. The loads of U splits for all of the
+    // lane's outputs are issued before any is added, so the merge costs one
+    // memory round trip per U splits instead of one per load. One-block
+    // wavefronts (the library's split-K plans, five or six splits) take all
+    // splits in one round trip (M = 16 down GEMM 2% faster); wider ones keep
+    // four, since the larger merge's registers slowed the M = 1 gate/up
+    // kernel, which shares the instantiation, by 13%.
+    constexpr int U = (NBW == 1) ? 8 : 4;
     const int64_t sstride = (int64_t)M * ga.n_total;
     const float* pp[NBW][4];
     bool ok[NBW][4];
