@@ -13,7 +13,7 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("words", [1, 3, 257, 4 * 256 * 7 + 5, (1 << 20) + 3])
-@pytest.mark.parametrize("wgs", [1, 7, 2048])
+@pytest.mark.parametrize("wgs", [1, 7, 2048, 65536])
 @pytest.mark.parametrize("where", ["none", "first", "last"])
 def test_probe_reads_every_word(words, wgs, where):
     print("read probe: words=%d workgroups=%d marker=%s" % (words, wgs, where), flush=True)
