@@ -54,6 +54,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only-headline", action="store_true", help="skip the other workloads")
+    ap.add_argument("--workload", default="",
+                    help="run only the other workloads whose key contains this text (tiny, "
+                         "verify, drafter, prefill, fp16act, pack, dequant, fake_quant, "
+                         "grouped, attention)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 256 MiB device copy (reference for HBM byte counters)")
@@ -502,19 +506,23 @@ def main():
     down.free()
     torch.cuda.empty_cache()
 
+    others = [("tiny", lambda: measure_workload(torch, q, 1)),
+              ("verify", lambda: measure_workload(torch, q, 3)),
+              ("drafter_w8a16", lambda: measure_workload(torch, q, 4)),
+              ("prefill", lambda: measure_workload(torch, q, 5)),
+              ("fp16act", lambda: measure_workload(torch, q, 2, act="f16")),
+              ("pack", lambda: measure_pack(torch, q)),
+              ("dequant", lambda: measure_dequant(torch, q)),
+              ("fake_quant", lambda: measure_fake_quant(torch, q)),
+              ("grouped_w8", lambda: measure_grouped(torch, q, 8)),
+              ("grouped_w4", lambda: measure_grouped(torch, q, 4))]
+    for B in (1, 8):
+        for w in (1024, 2048, 0):
+            others.append(("attention_b%d_w%d" % (B, w),
+                           lambda w=w, B=B: measure_attention(torch, q, w, B)))
     extra = []
     if not args.only_headline:
-        for cfg in (1, 3, 4, 5):
-            extra.append(measure_workload(torch, q, cfg))
-        extra.append(measure_workload(torch, q, 2, act="f16"))
-        extra.append(measure_pack(torch, q))
-        extra.append(measure_dequant(torch, q))
-        extra.append(measure_fake_quant(torch, q))
-        extra.append(measure_grouped(torch, q, 8))
-        extra.append(measure_grouped(torch, q, 4))
-        for B in (1, 8):
-            for w in (1024, 2048, 0):
-                extra.append(measure_attention(torch, q, w, B))
+        extra = [fn() for key, fn in others if args.workload in key]
 
     if args.copy_calibration:
         copy_calibration(torch)
