@@ -441,8 +441,15 @@ def cpu_baseline(seconds):
         if time.perf_counter() - t0 >= seconds:
             break
     dt = time.perf_counter() - t0
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+    except OSError:  # pragma: no cover
+        pass
     return {"value": round(nbytes * n / dt / 1e9, 3), "unit": "GB/s", "cores": blas_threads,
-            "kind": "oracle",
+            "kind": "oracle", "blas_threads": blas_threads, "host_cpus": os.cpu_count() or 0,
+            "cpu_model": model,
             "sample": "%d full decode steps (gate/up 2560x19456 + down 9728x2560, M=1): "
                       "float64 dequantization + float64 matmul, %.1f s; host has %d CPUs"
                       % (n, dt, os.cpu_count() or 0)}
