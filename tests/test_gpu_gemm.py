@@ -265,3 +265,19 @@ def test_workloads_full_size(cfg, shape_index):
         ok = gemm.within_tolerance(got, ref, ref_rms=0.9 * gemm.rms(ref))
         assert ok.all(), (int((~ok).sum()), got[~ok][:5], ref[~ok][:5])
         assert np.all(np.isfinite(numerics.bf16_to_f64(got_bits)))
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("M", [1, 16, 300])
+def test_heavy_tailed_weights_through_rtn(bits, M):
+    """Heavy-tailed weights (Student-t, 3 dof, x 0.02): the oracle's RTN scales
+    and Q_s codes, whose scales then spread over a wide range across groups,
+    through the decode, verification and prefill paths."""
+    K, N = 1280, 336
+    W = workloads.weights(K, N, 90 + M, dist="student_t")
+    sb = quant.rtn_scales(W, bits)
+    c = quant.q_s(W, numerics.scale_bits_to_f64(sb, SDT[bits]), bits)
+    x = workloads.activations(M, K, 91 + M)
+    sv = numerics.scale_bits_to_f64(sb, SDT[bits])
+    assert sv.max() / sv[sv > 0].min() > 8        # the scales do spread
+    _assert_close(_run(bits, x, c, sb, N), gemm.gemm_ref(x, c, sb, SDT[bits]), "M=%d" % M)
