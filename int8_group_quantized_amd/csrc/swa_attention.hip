@@ -24,8 +24,9 @@
 //                 give the 8 keys a lane supplies), A = V^T read from a
 //                 per-wavefront LDS copy of the step's 32 value rows with
 //                 gfx950's transposing LDS read: in each group of 16 lanes,
-//                 lane s names four consecutive 16-bit values (row s) and
-//                 lane t receives element t % 4 of rows t / 4 + 4e, e < 4.
+//                 lane s names four consecutive 16-bit values (row s of a
+//                 16 x 4 block) and lane t receives element t % 4 of block
+//                 rows t / 4 + 4e, e < 4.
 // P is split into a bf16 high part and the bf16 rounding of the remainder,
 // so P V is accumulated with ~2^-18 relative error in P (two instructions
 // per block) instead of bf16's 2^-9.
