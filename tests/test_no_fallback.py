@@ -40,3 +40,12 @@ def test_package_sources_do_not_reference_the_oracle():
             if f.endswith((".py", ".cpp", ".hip", ".h")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
+
+
+def test_oracle_does_not_reference_the_product():
+    odir = os.path.join(ROOT, "oracle")
+    for f in os.listdir(odir):
+        if f.endswith(".py"):
+            text = open(os.path.join(odir, f)).read()
+            assert "int8_group_quantized_amd" not in text, f
+            assert "libqgemm" not in text, f
