@@ -219,7 +219,10 @@ def qgemm(x, packed_w, scales, bits, N, out=None, plan=None, ws=None):
     both bf16 or both fp16 (qgemm_w*a16 / qgemm_w*f16 in the C ABI).
 
     plan: optional (cols_per_wave, k_waves, splits) for the small-M kernel.
-    ws: optional workspace tensor (zeroed before first use).
+    ws: optional workspace tensor (zeroed before first use). Without it the
+    call uses the device's shared workspace, which is safe for calls in
+    order on one stream; calls that may run concurrently on different
+    streams must each pass their own ws.
     """
     _need_cuda(x, packed_w, scales, out)
     if x.dtype not in (torch.bfloat16, torch.float16):
