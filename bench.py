@@ -129,12 +129,14 @@ class Weights:
         self.out = torch.empty((self.M, self.N), dtype=xdt, device="cuda")
         self.ws = torch.zeros(max(q.workspace_bytes(self.bits, self.M, self.K, self.N), 1 << 16),
                               dtype=torch.uint8, device="cuda")
+        self.cbm = False              # scales in the logical [K/128, N] order
         self.bytes = alg_bytes(self.bits, self.M, self.K, self.N)
         self.flops = 2 * self.M * self.K * self.N
 
     def call(self, q, i):
         j = i % len(self.packed)
-        q.qgemm(self.x, self.packed[j], self.scales[j], self.bits, self.N, out=self.out, ws=self.ws)
+        q.qgemm(self.x, self.packed[j], self.scales[j], self.bits, self.N, out=self.out, ws=self.ws,
+                scales_cbm=self.cbm)
 
     def free(self):
         self.W = None
@@ -224,6 +226,42 @@ def read_stream_ceiling(torch, q, bufs, widths=(1024, 2048, 4096, 8192, 16384)):
         if best is None or us < best[0]:
             best = (us, nbytes, wgs)
     return best
+
+
+def measure_decode_cbm(torch, q, steps=2000):
+    """The headline's decode step with the scales prepacked column-block-major
+    (qg_prepack_scales, done once like the codes): same weights, copies,
+    bytes and arithmetic (bit-identical outputs), only the scale order
+    differs. Context beside the headline, which uses the logical order."""
+    up = Weights(q, torch, 2, 0, copies_for(4, 2560, 19456))
+    down = Weights(q, torch, 2, 1, copies_for(4, 9728, 2560))
+    up.W = down.W = None
+    for wt in (up, down):
+        wt.scales = [q.prepack_scales(s) for s in wt.scales]
+        wt.cbm = True
+    torch.cuda.empty_cache()
+
+    def step(i):
+        up.call(q, i)
+        down.call(q, i)
+
+    graphs = graphs_for_steps(torch, step, steps)
+    for g in set(graphs):
+        g.replay()
+    ms = time_graphs(torch, graphs) / steps
+    k_ms = kernel_average(torch, up, q)
+    step_bytes = up.bytes + down.bytes
+    gbs = step_bytes / (ms * 1e-3) / 1e9
+    k_gbs = up.bytes / (k_ms * 1e-3) / 1e9
+    del graphs
+    up.free()
+    down.free()
+    torch.cuda.empty_cache()
+    return {"workload": "decode_w4a16_m1, scales column-block-major (qg_prepack_scales)",
+            "us_per_step": round(ms * 1e3, 3), "gbs": round(gbs, 1),
+            "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "gate_up_us_per_launch": round(k_ms * 1e3, 3),
+            "gate_up_frac_hbm_peak": round(k_gbs / HBM_PEAK_GBS, 4)}
 
 
 def dense_bf16_reference(torch, M, K, N, reps=10):
@@ -513,7 +551,8 @@ def main():
     down.free()
     torch.cuda.empty_cache()
 
-    others = [("tiny", lambda: measure_workload(torch, q, 1)),
+    others = [("decode_cbm", lambda: measure_decode_cbm(torch, q)),
+              ("tiny", lambda: measure_workload(torch, q, 1)),
               ("verify", lambda: measure_workload(torch, q, 3)),
               ("drafter_w8a16", lambda: measure_workload(torch, q, 4)),
               ("prefill", lambda: measure_workload(torch, q, 5)),

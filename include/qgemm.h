@@ -71,7 +71,12 @@ typedef enum {
   QG_ERR_PLAN = 7       /* an explicit tiling plan is not supported        */
 } qg_status;
 
-typedef enum { QG_BF16 = 0, QG_F16 = 1, QG_F32 = 2 } qg_dtype;
+/* Element types. The *_CBM values name scales (fp16 or bf16) stored
+ * column-block-major by qg_prepack_scales; only the GEMM entry points accept
+ * them (every other entry point returns QG_ERR_DTYPE). */
+typedef enum {
+  QG_BF16 = 0, QG_F16 = 1, QG_F32 = 2, QG_F16_CBM = 3, QG_BF16_CBM = 4
+} qg_dtype;
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* qg_status_str(qg_status s);
@@ -320,6 +325,23 @@ qg_status qg_swa_attention_chunk(const void* q, const void* k_cache, const void*
                                  int64_t Hq, int64_t Hkv, int64_t D, int64_t S_max,
                                  int64_t window, float scale, int64_t chunk, void* workspace,
                                  size_t workspace_bytes, void* stream);
+
+/* Column-block-major scales: a storage order of the same scales, prepared
+ * once at load time like the packed codes. The logical scales[K/128, N]
+ * (group g, column n) become cbm[N/16][K/128][16] with
+ *   cbm[((n / 16) * (K / 128) + g) * 16 + n % 16] = scales[g * N + n],
+ * so the scales of one 16-column block for every group are one contiguous
+ * run (the layout is the library's own; the pages fix none). A small-M GEMM
+ * workgroup then reads its scales as one run instead of gathering one piece
+ * per group from rows N * 2 bytes apart, which delays its first multiply
+ * (about 0.3 µs of the 8 µs decode GEMV on MI355X). Pass the result to the
+ * GEMM entry points with s_dt = QG_F16_CBM or QG_BF16_CBM; their outputs
+ * are bit-identical to those with the logical scales.
+ *   scales  [K/128, N] logical, s_dt = QG_F16 or QG_BF16
+ *   out     K/128 * N elements of s_dt (not in place)
+ * K and N follow the shape rules above. */
+qg_status qg_prepack_scales(const void* scales, qg_dtype s_dt, int64_t K, int64_t N,
+                            void* out, void* stream);
 
 /* Read-stream probe: a measurement aid, not a step of the method. Reads
  * [src, src + bytes) once with 16-byte nontemporal vector loads over

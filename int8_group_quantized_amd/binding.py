@@ -19,6 +19,8 @@ _lib = None
 _lock = threading.Lock()
 
 QG_BF16, QG_F16, QG_F32 = 0, 1, 2
+QG_F16_CBM, QG_BF16_CBM = 3, 4           # column-block-major scales (prepack_scales)
+_CBM = {QG_F16: QG_F16_CBM, QG_BF16: QG_BF16_CBM}
 STATUS = {0: "QG_OK", 1: "QG_ERR_NULL", 2: "QG_ERR_SHAPE", 3: "QG_ERR_ALIGN",
           4: "QG_ERR_DTYPE", 5: "QG_ERR_WORKSPACE", 6: "QG_ERR_HIP", 7: "QG_ERR_PLAN"}
 
@@ -76,6 +78,7 @@ _SIGNATURES = {
     "qg_swa_attention_chunk": ([_P, _P, _P, _P, _P] + [_I64] * 7 + [ctypes.c_float, _I64, _P, _SZ,
                                                                      _P], _INT),
     "qg_read_stream": ([_P, _SZ, _INT, _P, _P], _INT),
+    "qg_prepack_scales": ([_P, _INT, _I64, _I64, _P, _P], _INT),
 }
 
 
@@ -214,7 +217,28 @@ def unpack(packed, K, N, bits):
     return codes
 
 
-def qgemm(x, packed_w, scales, bits, N, out=None, plan=None, ws=None):
+def _sdt(scales, cbm):
+    d = _dt(scales)
+    if cbm:
+        if scales.dim() != 3 or scales.shape[2] != 16:
+            raise ValueError("column-block-major scales come from prepack_scales ([N/16, K/128, 16])")
+        return _CBM[d]
+    return d
+
+
+def prepack_scales(scales):
+    """Column-block-major copy of scales [K/128, N] (qg_prepack_scales),
+    shaped [N/16, K/128, 16]; pass it with scales_cbm=True to qgemm or
+    qgemm_grouped, whose outputs equal those with the logical scales."""
+    _need_cuda(scales)
+    G, N = scales.shape
+    out = torch.empty((N // 16, G, 16), dtype=scales.dtype, device=scales.device)
+    _check("qg_prepack_scales", lib().qg_prepack_scales(_ptr(scales), _dt(scales), G * 128, N,
+                                                        _ptr(out), _stream(scales)))
+    return out
+
+
+def qgemm(x, packed_w, scales, bits, N, out=None, plan=None, ws=None, scales_cbm=False):
     """out[M,N] = x[M,K] . (s (.) W_q) with fp32 accumulation; x and out are
     both bf16 or both fp16 (qgemm_w*a16 / qgemm_w*f16 in the C ABI).
 
@@ -223,6 +247,7 @@ def qgemm(x, packed_w, scales, bits, N, out=None, plan=None, ws=None):
     call uses the device's shared workspace, which is safe for calls in
     order on one stream; calls that may run concurrently on different
     streams must each pass their own ws.
+    scales_cbm: scales come from prepack_scales (column-block-major).
     """
     _need_cuda(x, packed_w, scales, out)
     if x.dtype not in (torch.bfloat16, torch.float16):
@@ -239,13 +264,13 @@ def qgemm(x, packed_w, scales, bits, N, out=None, plan=None, ws=None):
     ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
     if plan is None:
         fn = "qgemm_w%d%s" % (bits, act)
-        code = getattr(lib(), fn)(_ptr(x), _ptr(packed_w), _ptr(scales), _dt(scales), _ptr(out),
-                                  M, K, N, _ptr(ws), ws_bytes, _stream(x))
+        code = getattr(lib(), fn)(_ptr(x), _ptr(packed_w), _ptr(scales), _sdt(scales, scales_cbm),
+                                  _ptr(out), M, K, N, _ptr(ws), ws_bytes, _stream(x))
     else:
         fn = "qgemm_w%d%s_plan" % (bits, act)
-        code = getattr(lib(), fn)(_ptr(x), _ptr(packed_w), _ptr(scales), _dt(scales), _ptr(out),
-                                  M, K, N, _ptr(ws), ws_bytes, plan[0], plan[1], plan[2],
-                                  _stream(x))
+        code = getattr(lib(), fn)(_ptr(x), _ptr(packed_w), _ptr(scales), _sdt(scales, scales_cbm),
+                                  _ptr(out), M, K, N, _ptr(ws), ws_bytes, plan[0], plan[1],
+                                  plan[2], _stream(x))
     _check(fn, code)
     return out
 
@@ -295,7 +320,7 @@ class FakeQuantSTE(torch.autograd.Function):
         return grad, None, None
 
 
-def qgemm_grouped(x, weights, bits, outs=None, ws=None):
+def qgemm_grouped(x, weights, bits, outs=None, ws=None, scales_cbm=False):
     """One launch of several GEMMs sharing x: weights is a list of
     (packed_w, scales, N); returns the list of outputs [M, N_i]."""
     _need_cuda(x)
@@ -313,7 +338,7 @@ def qgemm_grouped(x, weights, bits, outs=None, ws=None):
         ws = workspace(x.device, need)
     ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
     fn = "qgemm_w%d%s_grouped" % (bits, "a16" if x.dtype == torch.bfloat16 else "f16")
-    _check(fn, getattr(lib(), fn)(_ptr(x), items, len(weights), _dt(weights[0][1]), M, K,
+    _check(fn, getattr(lib(), fn)(_ptr(x), items, len(weights), _sdt(weights[0][1], scales_cbm), M, K,
                                   _ptr(ws), ws_bytes, _stream(x)))
     return outs
 

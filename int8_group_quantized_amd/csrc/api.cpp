@@ -43,7 +43,12 @@ qg_status check_ptrs(std::initializer_list<const void*> ptrs) {
 
 qg_status from_hip(hipError_t e) { return e == hipSuccess ? QG_OK : QG_ERR_HIP; }
 
-bool s_bf16(qg_dtype d) { return d == QG_BF16; }
+bool s_bf16(qg_dtype d) { return d == QG_BF16 || d == QG_BF16_CBM; }
+// Scale dtypes the GEMM entry points take: logical or column-block-major.
+bool gemm_scale_dtype(qg_dtype d) {
+  return d == QG_F16 || d == QG_BF16 || d == QG_F16_CBM || d == QG_BF16_CBM;
+}
+bool s_cbm(qg_dtype d) { return d == QG_F16_CBM || d == QG_BF16_CBM; }
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
@@ -86,7 +91,7 @@ qg_status gemm(int bits, bool x_f16, const void* x, const void* packed, const vo
                size_t ws_bytes, int nbw, int wk, int splits, void* stream) {
   qg_status s = check_mkn(M, K, N);
   if (s != QG_OK) return s;
-  if (s_dt != QG_F16 && s_dt != QG_BF16) return QG_ERR_DTYPE;
+  if (!gemm_scale_dtype(s_dt)) return QG_ERR_DTYPE;
   if ((s = check_ptrs({packed, scales})) != QG_OK) return s;
   if (M == 0) return QG_OK;
   if ((s = check_ptrs({x, out})) != QG_OK) return s;
@@ -99,7 +104,8 @@ qg_status gemm(int bits, bool x_f16, const void* x, const void* packed, const vo
       if (ws == nullptr || ws_bytes < need) return QG_ERR_WORKSPACE;
       if (!aligned16(ws)) return QG_ERR_ALIGN;
     }
-    return from_hip(qg::launch_gemm_prefill(bits, pp, x, x_f16, packed, scales, s_bf16(s_dt), out,
+    return from_hip(qg::launch_gemm_prefill(bits, pp, x, x_f16, packed, scales, s_bf16(s_dt),
+                                            s_cbm(s_dt), out,
                                             M, K, N, ws, as_stream(stream)));
   }
   qg::SmallPlan plan;
@@ -116,7 +122,7 @@ qg_status gemm(int bits, bool x_f16, const void* x, const void* packed, const vo
   g.item[0].scales = static_cast<const uint16_t*>(scales);
   g.item[0].out = static_cast<uint16_t*>(out);
   qg::small_plan_group(plan, &g);
-  return from_hip(qg::launch_gemm_small(bits, plan, x, x_f16, g, s_bf16(s_dt), M, K, ws,
+  return from_hip(qg::launch_gemm_small(bits, plan, x, x_f16, g, s_bf16(s_dt), s_cbm(s_dt), M, K, ws,
                                         as_stream(stream)));
 }
 
@@ -168,7 +174,7 @@ size_t grouped_workspace(int bits, int64_t M, int64_t K, const qg_group_item* it
 qg_status gemm_grouped(int bits, bool x_f16, const void* x, const qg_group_item* items, int count,
                        qg_dtype s_dt, int64_t M, int64_t K, void* ws, size_t ws_bytes,
                        void* stream) {
-  if (s_dt != QG_F16 && s_dt != QG_BF16) return QG_ERR_DTYPE;
+  if (!gemm_scale_dtype(s_dt)) return QG_ERR_DTYPE;
   qg::SmallPlan plan;
   qg::GroupArgs g;
   qg_status s = grouped_plan(bits, M, K, items, count, &plan, &g);
@@ -189,13 +195,14 @@ qg_status gemm_grouped(int bits, bool x_f16, const void* x, const qg_group_item*
       qg::PrefillPlan pp;
       if (!qg::make_prefill_plan(M, K, items[i].N, &pp)) return QG_ERR_SHAPE;
       s = from_hip(qg::launch_gemm_prefill(bits, pp, x, x_f16, items[i].packed_w, items[i].scales,
-                                           s_bf16(s_dt), items[i].out, M, K, items[i].N, ws,
+                                           s_bf16(s_dt), s_cbm(s_dt), items[i].out, M, K,
+                                           items[i].N, ws,
                                            as_stream(stream)));
       if (s != QG_OK) return s;
     }
     return QG_OK;
   }
-  return from_hip(qg::launch_gemm_small(bits, plan, x, x_f16, g, s_bf16(s_dt), M, K, ws,
+  return from_hip(qg::launch_gemm_small(bits, plan, x, x_f16, g, s_bf16(s_dt), s_cbm(s_dt), M, K, ws,
                                         as_stream(stream)));
 }
 
@@ -488,6 +495,15 @@ qg_status qg_swa_attention_chunk(const void* q, const void* k_cache, const void*
                                  size_t workspace_bytes, void* stream) {
   return swa_attention(q, k_cache, v_cache, seq_lens, out, B, T, Hq, Hkv, D, S_max, window,
                        scale, chunk, workspace, workspace_bytes, stream);
+}
+
+qg_status qg_prepack_scales(const void* scales, qg_dtype s_dt, int64_t K, int64_t N, void* out,
+                            void* stream) {
+  qg_status s = check_kn(K, N);
+  if (s != QG_OK) return s;
+  if (s_dt != QG_F16 && s_dt != QG_BF16) return QG_ERR_DTYPE;
+  if ((s = check_ptrs({scales, out})) != QG_OK) return s;
+  return from_hip(qg::launch_prepack_scales(scales, K, N, out, as_stream(stream)));
 }
 
 qg_status qg_read_stream(const void* src, size_t bytes, int workgroups, void* sink, void* stream) {

@@ -75,7 +75,7 @@ __device__ __forceinline__ void load_stage(char* st, const uint16_t* __restrict_
                                            const uint16_t* __restrict__ scales,
                                            const float* __restrict__ nbias, int g, int wave,
                                            int lane, int m0, int cb0, int M, int K, int N, int NB,
-                                           int G, int Mp) {
+                                           int G, int Mp, int scbm) {
   using S = Stage<BITS, WN, NST>;
 #pragma unroll
   for (int i = 0; i < S::kXLoads; ++i) {
@@ -98,7 +98,10 @@ __device__ __forceinline__ void load_stage(char* st, const uint16_t* __restrict_
     const void* src;
     if (lane < 8) {
       const int col = min(cb0 * 16 + 64 * wave + 8 * lane, N - 8);
-      src = scales + (int64_t)g * N + col;
+      // Logical scales: row g of [G, N]; column-block-major: the run of the
+      // column's 16-wide block (qg_prepack_scales).
+      src = scbm ? scales + ((int64_t)(col >> 4) * G + g) * 16 + (col & 15)
+                 : scales + (int64_t)g * N + col;
     } else {
       src = nbias + (int64_t)g * Mp + m0 + S::kRowsPerWave * wave + 4 * (lane - 8);
     }
@@ -110,7 +113,7 @@ template <int BITS, bool SBF, bool XH, int WN, int NST>
 __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(2))) void gemm_prefill_kernel(
     const uint16_t* __restrict__ x, const char* __restrict__ packed,
     const uint16_t* __restrict__ scales, const float* __restrict__ nbias,
-    uint16_t* __restrict__ out, int M, int K, int N, int Mp, int tiles_n, int tiles) {
+    uint16_t* __restrict__ out, int M, int K, int N, int Mp, int tiles_n, int tiles, int scbm) {
   using S = Stage<BITS, WN, NST>;
   using A = Act<XH>;
   extern __shared__ u32x4 smem[];
@@ -166,7 +169,7 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(2))) vo
   for (int s = 0; s < NST - 1; ++s)
     if (s < G)
       load_stage<BITS, WN, NST>(lds + s * S::kBytes, x, packed, scales, nbias, s, wave, lane, m0,
-                                cb0, M, K, N, NB, G, Mp);
+                                cb0, M, K, N, NB, G, Mp, scbm);
 
   int cur = 0;   // ring slot of group g
   for (int g = 0; g < G; ++g) {
@@ -182,7 +185,7 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(2))) vo
     if (ahead < G) {
       const int slot = (cur == 0) ? NST - 1 : cur - 1;
       load_stage<BITS, WN, NST>(lds + slot * S::kBytes, x, packed, scales, nbias, ahead, wave,
-                                lane, m0, cb0, M, K, N, NB, G, Mp);
+                                lane, m0, cb0, M, K, N, NB, G, Mp, scbm);
     }
     const char* st = lds + cur * S::kBytes;
     cur = (cur == NST - 1) ? 0 : cur + 1;
@@ -298,17 +301,17 @@ __global__ __launch_bounds__(256) void prefill_bias_kernel(const uint16_t* __res
 
 template <int BITS, bool SBF, bool XH, int WN, int NST>
 void launch_main(const PrefillPlan& p, const uint16_t* x, const char* w, const uint16_t* s,
-                 const float* nb, uint16_t* out, int M, int K, int N, hipStream_t st) {
+                 const float* nb, uint16_t* out, int M, int K, int N, int scbm, hipStream_t st) {
   gemm_prefill_kernel<BITS, SBF, XH, WN, NST>
       <<<dim3((unsigned)p.tiles), 64 * WN, NST * Stage<BITS, WN, NST>::kBytes, st>>>(
-          x, w, s, nb, out, M, K, N, (int)p.mp, p.tiles_n, p.tiles);
+          x, w, s, nb, out, M, K, N, (int)p.mp, p.tiles_n, p.tiles, scbm);
 }
 
 template <int BITS, bool SBF, bool XH>
 void launch_bits(const PrefillPlan& p, const uint16_t* x, const char* w, const uint16_t* s,
-                 const float* nb, uint16_t* out, int M, int K, int N, hipStream_t st) {
-  if (p.wn == 4) launch_main<BITS, SBF, XH, 4, 2>(p, x, w, s, nb, out, M, K, N, st);
-  else           launch_main<BITS, SBF, XH, 2, 2>(p, x, w, s, nb, out, M, K, N, st);
+                 const float* nb, uint16_t* out, int M, int K, int N, int scbm, hipStream_t st) {
+  if (p.wn == 4) launch_main<BITS, SBF, XH, 4, 2>(p, x, w, s, nb, out, M, K, N, scbm, st);
+  else           launch_main<BITS, SBF, XH, 2, 2>(p, x, w, s, nb, out, M, K, N, scbm, st);
 }
 
 constexpr int kCUs = 256;   // MI355X compute units (plan heuristic only)
@@ -348,8 +351,10 @@ size_t prefill_workspace(int bits, const PrefillPlan& p, int64_t K) {
 }
 
 hipError_t launch_gemm_prefill(int bits, const PrefillPlan& p, const void* x, bool x_f16,
-                               const void* packed, const void* scales, bool s_bf16, void* out,
-                               int64_t M, int64_t K, int64_t N, void* ws, hipStream_t st) {
+                               const void* packed, const void* scales, bool s_bf16, bool s_cbm,
+                               void* out, int64_t M, int64_t K, int64_t N, void* ws,
+                               hipStream_t st) {
+  const int scbm = s_cbm ? 1 : 0;
   const auto* xp = static_cast<const uint16_t*>(x);
   const auto* wp = static_cast<const char*>(packed);
   const auto* sp = static_cast<const uint16_t*>(scales);
@@ -363,19 +368,19 @@ hipError_t launch_gemm_prefill(int bits, const PrefillPlan& p, const void* x, bo
     if (x_f16) prefill_bias_kernel<true><<<bgrid, 256, 0, st>>>(xp, nb, m, k, (int)p.mp, units);
     else       prefill_bias_kernel<false><<<bgrid, 256, 0, st>>>(xp, nb, m, k, (int)p.mp, units);
     if (x_f16) {
-      if (s_bf16) launch_bits<4, true, true>(p, xp, wp, sp, nb, op, m, k, n, st);
-      else        launch_bits<4, false, true>(p, xp, wp, sp, nb, op, m, k, n, st);
+      if (s_bf16) launch_bits<4, true, true>(p, xp, wp, sp, nb, op, m, k, n, scbm, st);
+      else        launch_bits<4, false, true>(p, xp, wp, sp, nb, op, m, k, n, scbm, st);
     } else {
-      if (s_bf16) launch_bits<4, true, false>(p, xp, wp, sp, nb, op, m, k, n, st);
-      else        launch_bits<4, false, false>(p, xp, wp, sp, nb, op, m, k, n, st);
+      if (s_bf16) launch_bits<4, true, false>(p, xp, wp, sp, nb, op, m, k, n, scbm, st);
+      else        launch_bits<4, false, false>(p, xp, wp, sp, nb, op, m, k, n, scbm, st);
     }
   } else {
     if (x_f16) {
-      if (s_bf16) launch_bits<8, true, true>(p, xp, wp, sp, nullptr, op, m, k, n, st);
-      else        launch_bits<8, false, true>(p, xp, wp, sp, nullptr, op, m, k, n, st);
+      if (s_bf16) launch_bits<8, true, true>(p, xp, wp, sp, nullptr, op, m, k, n, scbm, st);
+      else        launch_bits<8, false, true>(p, xp, wp, sp, nullptr, op, m, k, n, scbm, st);
     } else {
-      if (s_bf16) launch_bits<8, true, false>(p, xp, wp, sp, nullptr, op, m, k, n, st);
-      else        launch_bits<8, false, false>(p, xp, wp, sp, nullptr, op, m, k, n, st);
+      if (s_bf16) launch_bits<8, true, false>(p, xp, wp, sp, nullptr, op, m, k, n, scbm, st);
+      else        launch_bits<8, false, false>(p, xp, wp, sp, nullptr, op, m, k, n, scbm, st);
     }
   }
   return hipGetLastError();

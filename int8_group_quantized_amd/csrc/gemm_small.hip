@@ -111,7 +111,8 @@ struct Batch {
 template <int BITS, bool SBF, bool XH, bool GR, int MR, int NBW, int WN, int WK>
 __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_small_kernel(
     const uint16_t* __restrict__ x, uint32_t* __restrict__ counters,
-    float* __restrict__ partials, int M, int K, int splits, int gps, int sg, const GroupArgs ga) {
+    float* __restrict__ partials, int M, int K, int splits, int gps, int sg, int scbm,
+    const GroupArgs ga) {
   constexpr int NT = 64 * WN * WK;
   constexpr int NW = WN * WK;
   constexpr int TB = Tile<BITS>::bytes;
@@ -287,8 +288,11 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_small_kernel(
           const int cc = e / (2 * sn);
           const int rem = e - cc * 2 * sn;
           const int cbw = min(((int)blockIdx.x - wg0) * CBW + cc, NB - 1);
-          const uint16_t* src = scales + (int64_t)(wg_g0 + s0 + (rem >> 1)) * N + cbw * 16 +
-                                8 * (rem & 1);
+          // Logical scales: row g of [G, N]; column-block-major: the
+          // block's run of G groups x 16 columns.
+          const int gg = wg_g0 + s0 + (rem >> 1);
+          const uint16_t* src = scbm ? scales + ((int64_t)cbw * G + gg) * 16 + 8 * (rem & 1)
+                                     : scales + (int64_t)gg * N + cbw * 16 + 8 * (rem & 1);
           __builtin_amdgcn_global_load_lds(
               src, (__attribute__((address_space(3))) void*)(ss + w0), 16, 0, 0);
         }
@@ -472,8 +476,8 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_small_kernel(
 }
 
 template <int BITS, bool SBF, bool XH, bool GR, int MR, int NBW, int WN, int WK>
-hipError_t launch_variant(const SmallPlan& p, const void* x, const GroupArgs& g, int64_t M,
-                          int64_t K, void* ws, hipStream_t st) {
+hipError_t launch_variant(const SmallPlan& p, const void* x, const GroupArgs& g, bool s_cbm,
+                          int64_t M, int64_t K, void* ws, hipStream_t st) {
   const dim3 grid((unsigned)g.wg_total, (unsigned)p.splits, (unsigned)p.row_blocks);
   uint32_t* counters = nullptr;
   float* partials = nullptr;
@@ -484,27 +488,27 @@ hipError_t launch_variant(const SmallPlan& p, const void* x, const GroupArgs& g,
   const size_t lds = small_plan_lds_bytes(p, M);
   gemm_small_kernel<BITS, SBF, XH, GR, MR, NBW, WN, WK><<<grid, 64 * WN * WK, lds, st>>>(
       static_cast<const uint16_t*>(x), counters, partials, (int)M, (int)K, p.splits, p.gps,
-      p.sg, g);
+      p.sg, s_cbm ? 1 : 0, g);
   return hipGetLastError();
 }
 
 template <int BITS, bool SBF, bool XH, int MR>
-hipError_t launch_shape(const SmallPlan& p, const void* x, const GroupArgs& g, int64_t M,
-                        int64_t K, void* ws, hipStream_t st) {
+hipError_t launch_shape(const SmallPlan& p, const void* x, const GroupArgs& g, bool s_cbm,
+                        int64_t M, int64_t K, void* ws, hipStream_t st) {
   if (g.count > 1) {
     // Groups always take the library's own plan, which uses these shapes
     // (M = 1: one or two column blocks per wavefront, four K-wavefronts;
     // 2-16 rows: wide, long-K and the rest).
 #define QG_G(NBW, WN, WK)                                                                    \
     if (p.nbw == NBW && p.wn == WN && p.wk == WK)                                            \
-      return launch_variant<BITS, SBF, XH, true, MR, NBW, WN, WK>(p, x, g, M, K, ws, st);
+      return launch_variant<BITS, SBF, XH, true, MR, NBW, WN, WK>(p, x, g, s_cbm, M, K, ws, st);
     QG_G(1, 1, 4) QG_G(2, 1, 4) QG_G(2, 4, 1) QG_G(1, 4, 1)
 #undef QG_G
     return hipErrorInvalidValue;
   }
 #define QG_V(NBW, WN, WK)                                                                    \
   if (p.nbw == NBW && p.wn == WN && p.wk == WK)                                              \
-    return launch_variant<BITS, SBF, XH, false, MR, NBW, WN, WK>(p, x, g, M, K, ws, st);
+    return launch_variant<BITS, SBF, XH, false, MR, NBW, WN, WK>(p, x, g, s_cbm, M, K, ws, st);
   QG_V(1, 4, 1) QG_V(1, 2, 2) QG_V(1, 1, 4) QG_V(1, 1, 8)
   QG_V(2, 4, 1) QG_V(2, 1, 4)
   QG_V(4, 4, 1) QG_V(4, 1, 4)
@@ -618,11 +622,11 @@ void small_plan_group(const SmallPlan& p, GroupArgs* g) {
 }
 
 hipError_t launch_gemm_small(int bits, const SmallPlan& p, const void* x, bool x_f16,
-                             const GroupArgs& g, bool s_bf16, int64_t M, int64_t K, void* ws,
-                             hipStream_t st) {
+                             const GroupArgs& g, bool s_bf16, bool s_cbm, int64_t M, int64_t K,
+                             void* ws, hipStream_t st) {
 #define QG_B(B, S, H, R)                                                                  \
   if (bits == B && s_bf16 == S && x_f16 == H && p.mr == R)                                \
-    return launch_shape<B, S, H, R>(p, x, g, M, K, ws, st);
+    return launch_shape<B, S, H, R>(p, x, g, s_cbm, M, K, ws, st);
   QG_B(4, false, false, 1) QG_B(4, false, false, 16) QG_B(4, true, false, 1) QG_B(4, true, false, 16)
   QG_B(8, false, false, 1) QG_B(8, false, false, 16) QG_B(8, true, false, 1) QG_B(8, true, false, 16)
   QG_B(4, false, true, 1) QG_B(4, false, true, 16) QG_B(4, true, true, 1) QG_B(4, true, true, 16)

@@ -389,6 +389,21 @@ __global__ __launch_bounds__(256) void fake_quant_kernel(const void* __restrict_
 }
 
 
+// Scales [G, N] -> column-block-major [N/16][G][16]: a thread moves the 8
+// scales (16 bytes) at row g, columns 8p .. 8p+7 to their block's run.
+// Reads walk the rows contiguously; writes are whole 16-byte pieces.
+__global__ __launch_bounds__(256) void prepack_scales_kernel(const u32x4* __restrict__ in,
+                                                             u32x4* __restrict__ out, int G,
+                                                             int N) {
+  const int64_t piece = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int per_row = N / 8;
+  if (piece >= (int64_t)G * per_row) return;
+  const int g = (int)(piece / per_row);
+  const int c8 = (int)(piece - (int64_t)g * per_row);   // 8-column piece within the row
+  const int cb = c8 >> 1;                              // 16-column block
+  out[((int64_t)cb * G + g) * 2 + (c8 & 1)] = in[piece];
+}
+
 }  // namespace
 
 hipError_t launch_rtn_scales(int bits, const void* W, bool w_bf16, int64_t K, int64_t N,
@@ -427,6 +442,15 @@ hipError_t launch_prepack(int bits, const int8_t* codes, int64_t K, int64_t N, v
   const dim3 grid((unsigned)((N / kTileCols + 3) / 4), (unsigned)(K / kGroup));
   if (bits == 4) prepack_kernel<4><<<grid, 256, 0, st>>>(codes, packed, (int)K, (int)N);
   else           prepack_kernel<8><<<grid, 256, 0, st>>>(codes, packed, (int)K, (int)N);
+  return hipGetLastError();
+}
+
+hipError_t launch_prepack_scales(const void* scales, int64_t K, int64_t N, void* out,
+                                 hipStream_t st) {
+  const int64_t G = K / kGroup;
+  const int64_t pieces = G * (N / 8);
+  prepack_scales_kernel<<<(unsigned)((pieces + 255) / 256), 256, 0, st>>>(
+      static_cast<const u32x4*>(scales), static_cast<u32x4*>(out), (int)G, (int)N);
   return hipGetLastError();
 }
 

@@ -63,8 +63,9 @@ struct PrefillPlan {
 bool make_prefill_plan(int64_t M, int64_t K, int64_t N, PrefillPlan* plan);
 // Workspace bytes of the prefill path (INT4: counters area + negated offsets).
 size_t prefill_workspace(int bits, const PrefillPlan& p, int64_t K);
+// s_cbm: scales column-block-major (qg_prepack_scales) instead of [K/128, N].
 hipError_t launch_gemm_prefill(int bits, const PrefillPlan& p, const void* x, bool x_f16,
-                               const void* packed, const void* scales, bool s_bf16,
+                               const void* packed, const void* scales, bool s_bf16, bool s_cbm,
                                void* out, int64_t M, int64_t K, int64_t N, void* ws,
                                hipStream_t st);
 
@@ -91,8 +92,11 @@ hipError_t launch_dequant(int bits, const void* packed, const void* scales, bool
 // Fills the group's workgroup prefixes for plan p (wgs_n is per item there).
 void small_plan_group(const SmallPlan& p, GroupArgs* g);
 hipError_t launch_gemm_small(int bits, const SmallPlan& p, const void* x, bool x_f16,
-                             const GroupArgs& g, bool s_bf16, int64_t M, int64_t K,
+                             const GroupArgs& g, bool s_bf16, bool s_cbm, int64_t M, int64_t K,
                              void* workspace, hipStream_t st);
+// Logical scales [K/128, N] -> column-block-major [N/16][K/128][16] (16-bit).
+hipError_t launch_prepack_scales(const void* scales, int64_t K, int64_t N, void* out,
+                                 hipStream_t st);
 
 // Drafter sliding-window attention (swa_attention.hip): one workgroup per
 // (sequence, query head, chunk of `chunk` keys); `units` = sequences x KV heads

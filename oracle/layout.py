@@ -96,3 +96,18 @@ def unpack(packed, bits, K, N):
 def storage_bytes(bits, n_params, scale_bytes=2):
     """Bytes for n_params weights: the codes plus one 2-byte scale per 128."""
     return n_params * bits / 8 + n_params / GROUP * scale_bytes
+
+
+def scales_cbm(scales):
+    """Column-block-major order of scales [G, N] (the library's own storage
+    order for qg_prepack_scales; the pages fix none): element (g, n) moves to
+    flat position ((n // 16) * G + g) * 16 + n % 16, written out one element
+    at a time. Returns a flat array of the same dtype."""
+    G, N = scales.shape
+    if N % 16:
+        raise ValueError("N must be a multiple of 16")
+    out = np.empty(G * N, dtype=scales.dtype)
+    for g in range(G):
+        for n in range(N):
+            out[((n // 16) * G + g) * 16 + n % 16] = scales[g, n]
+    return out

@@ -246,3 +246,24 @@ def test_read_stream_bad_pointers():
     assert L.qg_read_stream(FAKE, 16, 1, 0, None) == NULL
     assert L.qg_read_stream(MIS, 16, 1, FAKE, None) == ALIGN
     assert L.qg_read_stream(FAKE, 16, 1, MIS, None) == ALIGN
+
+
+def test_prepack_scales_rejects_bad_arguments():
+    L = q.lib()
+    assert L.qg_prepack_scales(FAKE, 1, 100, 16, FAKE, None) == SHAPE
+    assert L.qg_prepack_scales(FAKE, 1, 128, 24, FAKE, None) == SHAPE
+    assert L.qg_prepack_scales(FAKE, 2, 128, 16, FAKE, None) == DTYPE      # fp32 scales
+    assert L.qg_prepack_scales(FAKE, 3, 128, 16, FAKE, None) == DTYPE      # already prepacked
+    assert L.qg_prepack_scales(0, 1, 128, 16, FAKE, None) == NULL
+    assert L.qg_prepack_scales(FAKE, 1, 128, 16, MIS, None) == ALIGN
+
+
+@pytest.mark.parametrize("cbm", [3, 4])
+def test_prepacked_scales_only_for_gemms(cbm):
+    """Only the GEMM entry points take column-block-major scales."""
+    L = q.lib()
+    assert L.qg_pack_to_grid_w4(FAKE, 2, FAKE, cbm, 128, 16, FAKE, None) == DTYPE
+    assert L.qg_dequant_w4(FAKE, FAKE, cbm, 128, 16, FAKE, 0, None) == DTYPE
+    assert L.qg_fake_quant_w4(FAKE, 2, FAKE, cbm, 128, 16, FAKE, 0, None) == DTYPE
+    assert _gemm(M=1, K=100, N=512, sdt=cbm) == SHAPE          # accepted dtype, shape checked
+    assert L.qgemm_w4a16(FAKE, FAKE, FAKE, 5, FAKE, 1, 256, 512, 0, 0, None) == DTYPE

@@ -110,3 +110,20 @@ def test_storage_model_matches_printed_sizes():
     assert (n + n / 64 * 2) / 2**20 > g["w8a16_on_disk_MB"] + 2
     # INT4 costs 0.515625 bytes per weight
     assert layout.storage_bytes(4, 128) == 66
+
+
+def test_scales_cbm_hand_derived_and_a_permutation():
+    """Hand-worked positions of the column-block-major scale order for G = 3,
+    N = 32: (g, n) -> ((n // 16) * 3 + g) * 16 + n % 16."""
+    G, N = 3, 32
+    s = np.arange(G * N, dtype=np.uint16).reshape(G, N)       # value = g * 32 + n
+    flat = layout.scales_cbm(s)
+    assert flat[0] == 0            # (0, 0)
+    assert flat[15] == 15          # (0, 15)
+    assert flat[16] == 32          # (1, 0): block 0, group 1
+    assert flat[47] == 79          # (2, 15)
+    assert flat[48] == 16          # (0, 16): block 1 starts after 3 groups of block 0
+    assert flat[95] == 95          # (2, 31)
+    assert sorted(flat.tolist()) == list(range(G * N))         # a permutation
+    with pytest.raises(ValueError):
+        layout.scales_cbm(np.zeros((2, 24), dtype=np.uint16))
