@@ -20,7 +20,8 @@
  *   - Logical layouts are row-major and contiguous:
  *       x[M,K] bf16 (fp16 for the *f16 GEMMs), out[M,N] likewise,
  *       W[K,N], codes[K,N] int8,
- *       scales[K/128, N] (fp16 or bf16).
+ *       scales[K/128, N] (fp16 or bf16); the GEMM entry points also
+ *       take the column-block-major order of qg_prepack_scales.
  *     A PyTorch Linear weight is [N,K]; transpose it before packing.
  *   - K must be a positive multiple of 128 and N a positive multiple of 16,
  *     else QG_ERR_SHAPE. M may be 0 (nothing is launched). Limits:
