@@ -17,7 +17,8 @@ Besides the headline line, the same JSON object carries
   roofline      the dominant kernel (gate/up GEMV), timed live with events,
                 with the read-stream ceiling of one launch over the same
                 weight copies (the library's read probe) as context;
-  cpu_baseline  the CPU oracle timed on a bounded sample of the same step;
+  cpu_baseline  the CPU oracle timed on a bounded sample of the same step
+                (all BLAS threads; single_thread_value on one thread);
   workloads     the other shapes (the tiny 256 x 512 case, M=16
                 verification, W8A16 drafter, M=8192 prefill, fp16
                 activations, Q_s packing, dense dequantization, the fake
@@ -25,7 +26,14 @@ Besides the headline line, the same JSON object carries
                 sliding-window attention), each with its roofline fraction
                 (none for the tiny case, whose weights stay in cache); the
                 prefill rows also carry, as context, the vendor library's
-                dense bf16 GEMM (torch.matmul) at the same shape.
+                dense bf16 GEMM (torch.matmul) at the same shape. The M = 16
+                W4A16 and W8A16 sets are also run back to back (QKV, gate/up,
+                down) for their byte-weighted aggregate rate. Each row carries
+                the CPU oracle's figure for the same shape (cpu_oracle).
+
+The headline times exactly --steps steps after about 20 ms of untimed graph
+replays, like every other row: a short region timed cold reads up to ~15%
+slow while the GPU clocks settle.
 """
 
 import argparse
@@ -58,7 +66,7 @@ def parse():
                     help="run only the other workloads whose key contains this text (tiny, "
                          "verify, drafter, prefill, fp16act, pack, dequant, fake_quant, "
                          "grouped, attention)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 256 MiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
@@ -192,6 +200,17 @@ def time_steady(torch, g, reps, warm_ms=20.0):
     return time_graphs(torch, [g], reps=reps)
 
 
+def time_steps(torch, graphs, steps, warm_ms=20.0):
+    """Milliseconds per step over exactly `steps` steps (one replay of the
+    list of graphs), timed after untimed replays of the same graphs that keep
+    the GPU busy for about warm_ms (as time_steady does for one graph)."""
+    first = time_graphs(torch, graphs)
+    extra = min(1000, int(warm_ms / max(first, 1e-3)))
+    if extra:
+        time_graphs(torch, graphs, reps=extra)
+    return time_graphs(torch, graphs) / steps
+
+
 def graphs_for_steps(torch, step, steps):
     full, rem = divmod(steps, GRAPH_CHUNK)
     gs = []
@@ -228,7 +247,7 @@ def read_stream_ceiling(torch, q, bufs, widths=(1024, 2048, 4096, 8192, 16384)):
     return best
 
 
-def measure_decode_cbm(torch, q, steps=2000):
+def measure_decode_cbm(torch, q, steps):
     """The headline's decode step with the scales prepacked column-block-major
     (qg_prepack_scales, done once like the codes): same weights, copies,
     bytes and arithmetic (bit-identical outputs), only the scale order
@@ -246,9 +265,7 @@ def measure_decode_cbm(torch, q, steps=2000):
         down.call(q, i)
 
     graphs = graphs_for_steps(torch, step, steps)
-    for g in set(graphs):
-        g.replay()
-    ms = time_graphs(torch, graphs) / steps
+    ms = time_steps(torch, graphs, steps)       # same steps and warm-up as the headline
     k_ms = kernel_average(torch, up, q)
     step_bytes = up.bytes + down.bytes
     gbs = step_bytes / (ms * 1e-3) / 1e9
@@ -322,6 +339,40 @@ def measure_workload(torch, q, cfg, reps=1000, act="bf16"):
         torch.cuda.empty_cache()
     name = w["name"] if act == "bf16" else w["name"].replace("a16", "a16_fp16act")
     return {"workload": name, "shapes": rows}
+
+
+def measure_set_sequence(torch, q, cfg, reps=400):
+    """A verification block's Linear set run back to back (fused QKV, gate/up,
+    down at M = 16, each over its own rotating weight copies), as one step
+    of a graph: the byte-weighted aggregate rate of the set (total
+    algorithmic bytes / time per step, launch gaps included)."""
+    import workloads
+    w = workloads.WORKLOADS[cfg]
+    order = [2, 0, 1]                     # QKV, gate/up, down
+    wts = []
+    for si in order:
+        K, N = w["shapes"][si]
+        wt = Weights(q, torch, cfg, si, copies_for(w["bits"], K, N))
+        wt.W = None
+        wts.append(wt)
+    torch.cuda.empty_cache()
+
+    def step(i):
+        for wt in wts:
+            wt.call(q, i)
+
+    g = capture(torch, step, 50)
+    ms = time_steady(torch, g, reps=max(1, reps // 50)) / (50 * max(1, reps // 50))
+    nbytes = sum(wt.bytes for wt in wts)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    for wt in wts:
+        wt.free()
+    del g
+    torch.cuda.empty_cache()
+    return {"workload": w["name"] + " set back to back (QKV, gate/up, down)",
+            "M": w["M"], "bits": w["bits"], "bytes_per_step": nbytes,
+            "us_per_step": round(ms * 1e3, 3), "gbs": round(gbs, 1),
+            "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
 
 
 def measure_pack(torch, q):
@@ -456,11 +507,7 @@ def cpu_baseline(seconds):
     """The oracle's product for the headline step, timed on the host."""
     from oracle import gemm, numerics, quant
     import workloads
-    try:
-        from threadpoolctl import threadpool_info
-        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        blas_threads = 1
+    blas_threads = _blas_threads()
     cases = []
     nbytes = 0
     for si, (K, N) in enumerate(workloads.WORKLOADS[2]["shapes"]):
@@ -493,6 +540,105 @@ def cpu_baseline(seconds):
                       % (n, dt, os.cpu_count() or 0)}
 
 
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        return 1
+
+
+def _median_seconds(fn, runs):
+    ts = []
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        fn()
+        ts.append(time.perf_counter() - t0)
+    return float(np.median(ts))
+
+
+def cpu_oracle_rows(rows_of_prefill=1024):
+    """The oracle's product (gemm_ref: exact dequantization and a float64
+    library matmul), timed on the host beside each GPU row: per shape of the
+    tiny, M = 16 W4A16 and W8A16 workloads, the median of 5 runs on all BLAS
+    threads and of 3 on one thread (the decode shapes' single-thread figure
+    is here too; their all-thread figure is the headline's cpu_baseline);
+    per prefill shape the median of 3 runs on a sample of the first
+    `rows_of_prefill` of the 8,192 rows (its GFLOP/s are for that sample).
+    Inputs come from the same seeds as the GPU rows."""
+    from oracle import gemm, numerics, quant
+    import workloads
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:  # pragma: no cover
+        threadpool_limits = None
+    threads = _blas_threads()
+    out = {}
+    for cfg in (1, 2, 3, 4, 5):
+        w = workloads.WORKLOADS[cfg]
+        bits, sdt = w["bits"], ("f16" if w["bits"] == 4 else "bf16")
+        for si, (K, N) in enumerate(w["shapes"]):
+            W = workloads.weights(K, N, workloads.seed_for(cfg, si, 0))
+            sb = quant.rtn_scales(W, bits)
+            codes = quant.q_s(W, numerics.scale_bits_to_f64(sb, sdt), bits)
+            del W
+            M = w["M"] if cfg != 5 else rows_of_prefill
+            x = workloads.activations(w["M"], K, workloads.seed_for(cfg, si, 1))[:M]
+            run = lambda: gemm.gemm_ref(x, codes, sb, sdt)
+            key = (cfg, si)
+            if cfg == 5:
+                t = _median_seconds(run, 3)
+                out[key] = {"gflops": round(2 * M * K * N / t / 1e9, 2), "s_per_call": round(t, 4),
+                            "threads": threads, "runs": 3,
+                            "sample": "first %d of %d rows" % (M, w["M"])}
+                continue
+            nbytes = alg_bytes(bits, M, K, N)
+            rec = {}
+            if cfg != 2:
+                t = _median_seconds(run, 5)
+                rec.update(gbs=round(nbytes / t / 1e9, 4), s_per_call=round(t, 4),
+                           threads=threads, runs=5)
+            if threadpool_limits is not None:
+                with threadpool_limits(limits=1):
+                    t1 = _median_seconds(run, 3)
+                rec.update(single_thread_gbs=round(nbytes / t1 / 1e9, 4),
+                           single_thread_s_per_call=round(t1, 4))
+            out[key] = rec
+    return out
+
+
+def attach_cpu_rows(extra, cpu):
+    """Put each oracle figure beside its GPU row (same config and shape)."""
+    import workloads
+    by_name = {workloads.WORKLOADS[c]["name"]: c for c in workloads.WORKLOADS}
+    for row in extra:
+        cfg = by_name.get(row.get("workload"))
+        if cfg is None:
+            continue
+        for si, shp in enumerate(row.get("shapes", [])):
+            rec = cpu.get((cfg, si))
+            if rec:
+                shp["cpu_oracle"] = rec
+    for row in extra:
+        name = row.get("workload", "")
+        for cfg in (3, 4):
+            if name.startswith(workloads.WORKLOADS[cfg]["name"] + " set"):
+                recs = [cpu.get((cfg, si)) for si in range(3)]
+                if all(r and "s_per_call" in r for r in recs):
+                    t = sum(r["s_per_call"] for r in recs)
+                    row["cpu_oracle"] = {"gbs": round(row["bytes_per_step"] / t / 1e9, 4),
+                                         "s_per_step": round(t, 4), "threads": recs[0]["threads"],
+                                         "sample": "sum of the three shapes' medians"}
+
+
+def log(msg):
+    """Progress line on stderr (the JSON result alone goes to stdout)."""
+    print("[bench %.1fs] %s" % (time.perf_counter() - _T0, msg), file=sys.stderr, flush=True)
+
+
+_T0 = time.perf_counter()
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -518,9 +664,10 @@ def main():
         step(i)
     torch.cuda.synchronize()
     graphs = graphs_for_steps(torch, step, args.steps)
-    for g in set(graphs):
-        g.replay()
-    ms = time_graphs(torch, graphs) / args.steps
+    # exactly args.steps steps, timed after ~20 ms of untimed replays of the
+    # same graphs (a short region timed cold reads up to ~15% slow while the
+    # clocks settle), as every other row is timed
+    ms = time_steps(torch, graphs, args.steps)
     step_bytes = up.bytes + down.bytes
     value = step_bytes / (ms * 1e-3) / 1e9
 
@@ -551,10 +698,12 @@ def main():
     down.free()
     torch.cuda.empty_cache()
 
-    others = [("decode_cbm", lambda: measure_decode_cbm(torch, q)),
+    others = [("decode_cbm", lambda: measure_decode_cbm(torch, q, args.steps)),
               ("tiny", lambda: measure_workload(torch, q, 1)),
               ("verify", lambda: measure_workload(torch, q, 3)),
+              ("verify_set", lambda: measure_set_sequence(torch, q, 3)),
               ("drafter_w8a16", lambda: measure_workload(torch, q, 4)),
+              ("drafter_w8a16_set", lambda: measure_set_sequence(torch, q, 4)),
               ("prefill", lambda: measure_workload(torch, q, 5)),
               ("fp16act", lambda: measure_workload(torch, q, 2, act="f16")),
               ("pack", lambda: measure_pack(torch, q)),
@@ -566,13 +715,25 @@ def main():
         for w in (1024, 2048, 0):
             others.append(("attention_b%d_w%d" % (B, w),
                            lambda w=w, B=B: measure_attention(torch, q, w, B)))
+    log("headline %.3f us per step, gate/up %.3f us per launch" % (ms * 1e3, k_ms * 1e3))
     extra = []
     if not args.only_headline:
-        extra = [fn() for key, fn in others if args.workload in key]
+        for key, fn in others:
+            if args.workload in key:
+                extra.append(fn())
+                log("row %s done" % key)
 
     if args.copy_calibration:
         copy_calibration(torch)
     cpu = None if args.no_cpu else cpu_baseline(args.cpu_seconds)
+    if cpu is not None:
+        log("cpu baseline done; timing the oracle beside each row")
+        rows = cpu_oracle_rows()
+        attach_cpu_rows(extra, rows)
+        single = rows.get((2, 0), {}), rows.get((2, 1), {})
+        if all("single_thread_s_per_call" in r for r in single):
+            t1 = sum(r["single_thread_s_per_call"] for r in single)
+            cpu["single_thread_value"] = round(step_bytes / t1 / 1e9, 4)
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 6),

@@ -11,5 +11,6 @@ from .binding import (  # noqa: F401
     QGError, lib, library_path, packed_bytes, workspace_bytes, rtn_scales,
     pack_to_grid, pack_to_grid_w4, pack_to_grid_w8, prepack, unpack, qgemm,
     qgemm_w4a16, qgemm_w8a16, dequant, fake_quant, FakeQuantSTE, qgemm_grouped,
-    swa_attention, read_stream, READ_PROBE_MARK, prepack_scales,
+    swa_attention, read_stream, READ_PROBE_MARK, prepack_scales, grouped_workspace_bytes,
+    check_weight,
 )

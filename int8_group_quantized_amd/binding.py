@@ -164,12 +164,31 @@ def workspace(device, nbytes):
     return ws
 
 
-def rtn_scales(W, bits):
-    """RTN scales [K/128, N]: fp16 (bits=4) or bf16 (bits=8)."""
-    _need_cuda(W)
+def _out_bytes(out, nbytes, what):
+    if out.numel() * out.element_size() != nbytes:
+        raise ValueError("%s must hold %d bytes" % (what, nbytes))
+
+
+def _check_scales(scales, K, N):
+    """Logical scales must be [K/128, N] (left to the library's status when
+    K or N is not a valid shape)."""
+    if K > 0 and N > 0 and K % 128 == 0 and N % 16 == 0 and tuple(scales.shape) != (K // 128, N):
+        raise ValueError("scales must be [K/128, N] = %s, got %s" % ((K // 128, N),
+                                                                     tuple(scales.shape)))
+
+
+def rtn_scales(W, bits, out=None):
+    """RTN scales [K/128, N]: fp16 (bits=4) or bf16 (bits=8), into out if given."""
+    _need_cuda(W, out)
     K, N = W.shape
-    s = torch.empty((K // 128, N), dtype=torch.float16 if bits == 4 else torch.bfloat16,
-                    device=W.device)
+    sdt = torch.float16 if bits == 4 else torch.bfloat16
+    if out is None:
+        s = torch.empty((K // 128, N), dtype=sdt, device=W.device)
+    else:
+        if out.dtype != sdt:
+            raise TypeError("out must be %s" % sdt)
+        _out_bytes(out, (K // 128) * N * 2, "out")
+        s = out
     fn = "qg_rtn_scales_w%d" % bits
     _check(fn, getattr(lib(), fn)(_ptr(W), _dt(W), K, N, _ptr(s), _stream(W)))
     return s
@@ -180,6 +199,7 @@ def pack_to_grid(W, scales, bits, out=None):
     given: a contiguous GPU tensor of packed_bytes(bits, K, N) bytes)."""
     _need_cuda(W, scales, out)
     K, N = W.shape
+    _check_scales(scales, K, N)
     if out is None:
         out = torch.empty(packed_bytes(bits, K, N), dtype=torch.uint8, device=W.device)
     elif out.numel() * out.element_size() != packed_bytes(bits, K, N):
@@ -198,20 +218,31 @@ def pack_to_grid_w8(W, scales):
     return pack_to_grid(W, scales, 8)
 
 
-def prepack(codes, bits):
-    _need_cuda(codes)
+def prepack(codes, bits, out=None):
+    _need_cuda(codes, out)
     if codes.dtype != torch.int8:
         raise TypeError("codes must be int8")
     K, N = codes.shape
-    out = torch.empty(packed_bytes(bits, K, N), dtype=torch.uint8, device=codes.device)
+    if out is None:
+        out = torch.empty(packed_bytes(bits, K, N), dtype=torch.uint8, device=codes.device)
+    else:
+        _out_bytes(out, packed_bytes(bits, K, N), "out")
     fn = "qg_prepack_w%d" % bits
     _check(fn, getattr(lib(), fn)(_ptr(codes), K, N, _ptr(out), _stream(codes)))
     return out
 
 
-def unpack(packed, K, N, bits):
-    _need_cuda(packed)
-    codes = torch.empty((K, N), dtype=torch.int8, device=packed.device)
+def unpack(packed, K, N, bits, out=None):
+    _need_cuda(packed, out)
+    if packed_bytes(bits, K, N):
+        _out_bytes(packed, packed_bytes(bits, K, N), "packed")
+    if out is None:
+        codes = torch.empty((K, N), dtype=torch.int8, device=packed.device)
+    else:
+        if out.dtype != torch.int8:
+            raise TypeError("out must be int8")
+        _out_bytes(out, K * N, "out")
+        codes = out
     fn = "qg_unpack_w%d" % bits
     _check(fn, getattr(lib(), fn)(_ptr(packed), K, N, _ptr(codes), _stream(packed)))
     return codes
@@ -219,20 +250,49 @@ def unpack(packed, K, N, bits):
 
 def _sdt(scales, cbm):
     d = _dt(scales)
-    if cbm:
-        if scales.dim() != 3 or scales.shape[2] != 16:
-            raise ValueError("column-block-major scales come from prepack_scales ([N/16, K/128, 16])")
-        return _CBM[d]
-    return d
+    if d not in _CBM:
+        raise TypeError("scales must be fp16 or bf16")
+    return _CBM[d] if cbm else d
 
 
-def prepack_scales(scales):
+def check_weight(packed_w, scales, bits, K, N, scales_cbm=False):
+    """Host-side agreement of a quantized weight with (bits, K, N): the packed
+    bytes are qg_packed_bytes(bits, K, N), and the scales are [K/128, N]
+    (logical order) or [N/16, K/128, 16] (column-block-major, from
+    prepack_scales, which must then be passed with scales_cbm=True). Shapes
+    the library rejects anyway (K not a multiple of 128, N of 16) are left
+    to its status code."""
+    if bits not in (4, 8):
+        raise ValueError("bits must be 4 or 8")
+    _sdt(scales, scales_cbm)
+    nb = packed_bytes(bits, K, N)
+    if nb == 0:
+        return
+    _out_bytes(packed_w, nb, "packed_w")
+    G = K // 128
+    if scales_cbm:
+        if tuple(scales.shape) != (N // 16, G, 16):
+            raise ValueError("column-block-major scales must be [N/16, K/128, 16] = %s, got %s"
+                             % ((N // 16, G, 16), tuple(scales.shape)))
+    else:
+        if scales.dim() == 3:
+            raise ValueError("3-D scales are the column-block-major order: pass scales_cbm=True")
+        if tuple(scales.shape) != (G, N):
+            raise ValueError("scales must be [K/128, N] = %s, got %s" % ((G, N), tuple(scales.shape)))
+
+
+def prepack_scales(scales, out=None):
     """Column-block-major copy of scales [K/128, N] (qg_prepack_scales),
     shaped [N/16, K/128, 16]; pass it with scales_cbm=True to qgemm or
     qgemm_grouped, whose outputs equal those with the logical scales."""
-    _need_cuda(scales)
+    _need_cuda(scales, out)
     G, N = scales.shape
-    out = torch.empty((N // 16, G, 16), dtype=scales.dtype, device=scales.device)
+    if out is None:
+        out = torch.empty((N // 16, G, 16), dtype=scales.dtype, device=scales.device)
+    else:
+        if out.dtype != scales.dtype:
+            raise TypeError("out must have the dtype of scales")
+        _out_bytes(out, G * N * 2, "out")
     _check("qg_prepack_scales", lib().qg_prepack_scales(_ptr(scales), _dt(scales), G * 128, N,
                                                         _ptr(out), _stream(scales)))
     return out
@@ -249,15 +309,20 @@ def qgemm(x, packed_w, scales, bits, N, out=None, plan=None, ws=None, scales_cbm
     streams must each pass their own ws.
     scales_cbm: scales come from prepack_scales (column-block-major).
     """
-    _need_cuda(x, packed_w, scales, out)
+    _need_cuda(x, packed_w, scales, out, ws)
     if x.dtype not in (torch.bfloat16, torch.float16):
         raise TypeError("x must be bf16 or fp16")
+    if x.dim() != 2:
+        raise ValueError("x must be [M, K]")
     act = "a16" if x.dtype == torch.bfloat16 else "f16"
     M, K = x.shape
+    check_weight(packed_w, scales, bits, K, N, scales_cbm)
     if out is None:
         out = torch.empty((M, N), dtype=x.dtype, device=x.device)
     elif out.dtype != x.dtype:
         raise TypeError("out must have the dtype of x")
+    elif tuple(out.shape) != (M, N):
+        raise ValueError("out must be [M, N] = %s" % ((M, N),))
     need = workspace_bytes(bits, M, K, N, plan)
     if ws is None and need > 0:
         ws = workspace(x.device, need)
@@ -275,19 +340,22 @@ def qgemm(x, packed_w, scales, bits, N, out=None, plan=None, ws=None, scales_cbm
     return out
 
 
-def qgemm_w4a16(x, packed_w, scales, N, out=None, plan=None, ws=None):
-    return qgemm(x, packed_w, scales, 4, N, out=out, plan=plan, ws=ws)
+def qgemm_w4a16(x, packed_w, scales, N, out=None, plan=None, ws=None, scales_cbm=False):
+    return qgemm(x, packed_w, scales, 4, N, out=out, plan=plan, ws=ws, scales_cbm=scales_cbm)
 
 
-def qgemm_w8a16(x, packed_w, scales, N, out=None, plan=None, ws=None):
-    return qgemm(x, packed_w, scales, 8, N, out=out, plan=plan, ws=ws)
+def qgemm_w8a16(x, packed_w, scales, N, out=None, plan=None, ws=None, scales_cbm=False):
+    return qgemm(x, packed_w, scales, 8, N, out=out, plan=plan, ws=ws, scales_cbm=scales_cbm)
 
 
 def dequant(packed_w, scales, bits, K, N, dtype=torch.bfloat16, out=None):
     """Dense W[K,N] = s (.) W_q, rounded once to dtype (bf16 or fp16)."""
     _need_cuda(packed_w, scales, out)
+    check_weight(packed_w, scales, bits, K, N)
     if out is None:
         out = torch.empty((K, N), dtype=dtype, device=packed_w.device)
+    elif tuple(out.shape) != (K, N):
+        raise ValueError("out must be [K, N]")
     fn = "qg_dequant_w%d" % bits
     _check(fn, getattr(lib(), fn)(_ptr(packed_w), _ptr(scales), _dt(scales), K, N, _ptr(out),
                                   _dt(out), _stream(packed_w)))
@@ -298,8 +366,11 @@ def fake_quant(W, scales, bits, dtype=None, out=None):
     """s (.) Q_s(W) rounded once to dtype (bf16, fp16 or fp32; default W's)."""
     _need_cuda(W, scales, out)
     K, N = W.shape
+    _check_scales(scales, K, N)
     if out is None:
         out = torch.empty((K, N), dtype=dtype or W.dtype, device=W.device)
+    elif tuple(out.shape) != (K, N):
+        raise ValueError("out must be [K, N]")
     fn = "qg_fake_quant_w%d" % bits
     _check(fn, getattr(lib(), fn)(_ptr(W), _dt(W), _ptr(scales), _dt(scales), K, N, _ptr(out),
                                   _dt(out), _stream(W)))
@@ -320,19 +391,42 @@ class FakeQuantSTE(torch.autograd.Function):
         return grad, None, None
 
 
+def _items(weights, outs=None):
+    return (GroupItem * len(weights))(*[
+        GroupItem(p.data_ptr(), sc.data_ptr(), outs[i].data_ptr() if outs is not None else 0, n)
+        for i, (p, sc, n) in enumerate(weights)])
+
+
+def grouped_workspace_bytes(bits, M, K, weights):
+    """Workspace bytes of a grouped call over weights [(packed_w, scales, N)]."""
+    items = _items(weights)
+    return int(lib().qg_workspace_bytes_grouped(bits, M, K, items, len(weights)))
+
+
 def qgemm_grouped(x, weights, bits, outs=None, ws=None, scales_cbm=False):
     """One launch of several GEMMs sharing x: weights is a list of
     (packed_w, scales, N); returns the list of outputs [M, N_i]."""
-    _need_cuda(x)
+    _need_cuda(x, ws)
     if x.dtype not in (torch.bfloat16, torch.float16):
         raise TypeError("x must be bf16 or fp16")
+    if x.dim() != 2:
+        raise ValueError("x must be [M, K]")
     M, K = x.shape
+    if not weights:
+        raise ValueError("weights is empty")
     if outs is None:
         outs = [torch.empty((M, n), dtype=x.dtype, device=x.device) for _, _, n in weights]
-    for (p, sc, _), o in zip(weights, outs):
+    if len(outs) != len(weights):
+        raise ValueError("one output per weight")
+    sdt = weights[0][1].dtype
+    for (p, sc, n), o in zip(weights, outs):
         _need_cuda(p, sc, o)
-    items = (GroupItem * len(weights))(*[GroupItem(p.data_ptr(), sc.data_ptr(), o.data_ptr(), n)
-                                         for (p, sc, n), o in zip(weights, outs)])
+        if sc.dtype != sdt:
+            raise TypeError("every item's scales must have one dtype (the ABI takes one)")
+        check_weight(p, sc, bits, K, n, scales_cbm)
+        if o.dtype != x.dtype or tuple(o.shape) != (M, n):
+            raise ValueError("each output must be [M, N_i] in the dtype of x")
+    items = _items(weights, outs)
     need = int(lib().qg_workspace_bytes_grouped(bits, M, K, items, len(weights)))
     if ws is None and need > 0:
         ws = workspace(x.device, need)

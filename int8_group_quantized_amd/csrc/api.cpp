@@ -86,15 +86,23 @@ qg_status unpack(int bits, const void* packed, int64_t K, int64_t N, int8_t* cod
   return from_hip(qg::launch_unpack(bits, packed, K, N, codes, as_stream(stream)));
 }
 
-qg_status gemm(int bits, bool x_f16, const void* x, const void* packed, const void* scales,
-               qg_dtype s_dt, void* out, int64_t M, int64_t K, int64_t N, void* ws,
-               size_t ws_bytes, int nbw, int wk, int splits, void* stream) {
+// The GEMM's argument checks other than the workspace (shape, scale dtype,
+// pointers), in the order the entry points report them.
+qg_status gemm_check(const void* x, const void* packed, const void* scales, qg_dtype s_dt,
+                     const void* out, int64_t M, int64_t K, int64_t N) {
   qg_status s = check_mkn(M, K, N);
   if (s != QG_OK) return s;
   if (!gemm_scale_dtype(s_dt)) return QG_ERR_DTYPE;
   if ((s = check_ptrs({packed, scales})) != QG_OK) return s;
   if (M == 0) return QG_OK;
-  if ((s = check_ptrs({x, out})) != QG_OK) return s;
+  return check_ptrs({x, out});
+}
+
+qg_status gemm(int bits, bool x_f16, const void* x, const void* packed, const void* scales,
+               qg_dtype s_dt, void* out, int64_t M, int64_t K, int64_t N, void* ws,
+               size_t ws_bytes, int nbw, int wk, int splits, void* stream) {
+  qg_status s = gemm_check(x, packed, scales, s_dt, out, M, K, N);
+  if (s != QG_OK || M == 0) return s;
   const bool explicit_plan = (nbw != 0 || wk != 0 || splits != 0);
   if (M > kSmallMaxM && !explicit_plan) {
     qg::PrefillPlan pp;

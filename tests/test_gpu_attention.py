@@ -8,6 +8,10 @@ it: scores are fp32 sums of exact bf16 products, the softmax runs in fp32,
 probabilities enter the value product as a bf16 pair (~2^-18 relative), the
 sums are fp32, and the one bf16 rounding of the output is 2^-9 relative.
 
+Every output is NaN-poisoned between canary bands, and the workspace's
+chunk results are NaN-poisoned before a canary band, so a query or head left
+unwritten, a chunk result never stored, or a stray store fails the test.
+
 Inputs: q, k, v ~ N(0, 1) rounded to bf16, seeded; the drafter's head layout
 (20 query heads, 4 KV heads of 128) and a 16-token block over the 8,192-token
 Long context, plus smaller ragged batches.
@@ -20,25 +24,30 @@ import torch
 import int8_group_quantized_amd as q
 from oracle import attention, numerics
 import workloads
-from gpu_helpers import DEV, dev_bf16, host_u16
+from gpu_helpers import DEV, Guarded, GuardedWorkspace, dev_bf16, host_u16
 
 pytestmark = pytest.mark.gpu
 
 D = 128
 
 
-def _run(B, T, Hq, Hkv, S_max, lens, window, seed, scale=None, chunk=0, std=1.0, poison=False):
+def _run(B, T, Hq, Hkv, S_max, lens, window, seed, scale=None, chunk=0, std=1.0, poison=False,
+         ws=None):
     qb, kb, vb = workloads.attention_inputs(B, T, Hq, Hkv, D, S_max, seed, std=std)
     if poison:   # NaN past each sequence's end: must never be read
         for b, S in enumerate(lens):
             kb[b, min(max(S, T), S_max):] = 0x7FC0
             vb[b, min(max(S, T), S_max):] = 0x7FC0
     sc = 1.0 / np.sqrt(D) if scale is None else scale
-    out = q.swa_attention(dev_bf16(qb), dev_bf16(kb), dev_bf16(vb),
-                          torch.tensor(lens, dtype=torch.int32, device=DEV), window, sc,
-                          chunk=chunk)
-    torch.cuda.synchronize()
-    return qb, kb, vb, sc, host_u16(out)
+    out = Guarded((B, T, Hq, D), torch.bfloat16)
+    wsg = ws or GuardedWorkspace(q.lib().qg_swa_workspace_bytes_chunk(B, T, Hq, Hkv, D, S_max,
+                                                                       window, chunk))
+    q.swa_attention(dev_bf16(qb), dev_bf16(kb), dev_bf16(vb),
+                    torch.tensor(lens, dtype=torch.int32, device=DEV), window, sc,
+                    chunk=chunk, out=out.t, ws=wsg.t)
+    got = out.check("attention")
+    wsg.check("attention")
+    return qb, kb, vb, sc, host_u16(got)
 
 
 def _ref(qb, kb, vb, lens, T, S_max, window, sc):
@@ -119,8 +128,9 @@ def test_scales_and_sharp_softmax(scale, std):
 def test_deterministic_and_workspace_reusable():
     lens = [2500, 1800]
     a = _parity(2, 16, 20, 4, 2500, lens, 0, 6800)
-    for _ in range(3):
-        _, _, _, _, b = _run(2, 16, 20, 4, 2500, lens, 0, 6800)
+    ws = GuardedWorkspace(q.lib().qg_swa_workspace_bytes_chunk(2, 16, 20, 4, D, 2500, 0, 0))
+    for _ in range(3):     # one workspace reused: its counters are left at zero
+        _, _, _, _, b = _run(2, 16, 20, 4, 2500, lens, 0, 6800, ws=ws)
         np.testing.assert_array_equal(a, b)
 
 

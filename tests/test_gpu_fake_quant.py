@@ -6,7 +6,9 @@ weight, scale and output format, on crafted cases (exact ties, clamp ends,
 zero scales, NaN / infinite / subnormal weights) and at full size; it also
 agrees with pack_to_grid followed by dequant (two independent GPU paths to
 s (.) Q_s(W)). The backward is the identity on the gradient (the straight-
-through estimator of the QAD paragraph).
+through estimator of the QAD paragraph). Outputs are NaN-poisoned (the
+fake quantizer never produces NaN: a NaN weight maps to code 0) between
+canary bands, so an unwritten element or a stray store fails the test.
 """
 
 import numpy as np
@@ -16,7 +18,7 @@ import torch
 import int8_group_quantized_amd as q
 from oracle import numerics, quant
 import workloads
-from gpu_helpers import DEV, dev_bf16, dev_f32, dev_scales, host_u16
+from gpu_helpers import DEV, Guarded, dev_bf16, dev_f32, dev_scales, host_u16
 
 pytestmark = pytest.mark.gpu
 
@@ -37,9 +39,16 @@ def _crafted(bits, K=256, N=64, seed=5):
     return W, sb
 
 
+def _fq(Wd, sd, bits, out_dt):
+    """fake_quant into a NaN-poisoned, guarded output."""
+    g = Guarded(tuple(Wd.shape), TDT[out_dt])
+    q.fake_quant(Wd, sd, bits, out=g.t)
+    return g.check("fake quant")
+
+
 def _gpu(W, w_dt, sb, bits, out_dt):
     Wd = dev_f32(W) if w_dt == "f32" else dev_bf16(workloads.to_bf16_bits(W))
-    out = q.fake_quant(Wd, dev_scales(sb, SDT[bits]), bits, dtype=TDT[out_dt])
+    out = _fq(Wd, dev_scales(sb, SDT[bits]), bits, out_dt)
     if out_dt == "f32":
         return out.cpu().numpy()
     return host_u16(out)
@@ -74,7 +83,7 @@ def test_shapes_and_other_scale_dtype(bits, K, N):
     other = "bf16" if bits == 4 else "f16"
     sb = workloads.scales(K // 128, N, other, K)
     Wd = dev_f32(W)
-    got = host_u16(q.fake_quant(Wd, dev_scales(sb, other), bits, dtype=torch.bfloat16))
+    got = host_u16(_fq(Wd, dev_scales(sb, other), bits, "bf16"))
     want = quant.fake_quant(W, sb, other, bits, "bf16")
     assert np.array_equal(got, want)
 
@@ -85,7 +94,7 @@ def test_maximum_extents(bits, K, N):
     """The largest K and N the boundary accepts (2^20), bit-exact."""
     W = workloads.weights(K, N, 13 + (K >> 7))
     sb = quant.rtn_scales(W, bits)
-    got = host_u16(q.fake_quant(dev_f32(W), dev_scales(sb, SDT[bits]), bits, dtype=torch.bfloat16))
+    got = host_u16(_fq(dev_f32(W), dev_scales(sb, SDT[bits]), bits, "bf16"))
     assert np.array_equal(got, quant.fake_quant(W, sb, SDT[bits], bits, "bf16"))
 
 
@@ -95,8 +104,10 @@ def test_equals_pack_then_dequant(bits):
     W = workloads.weights(K, N, 77)
     Wd = dev_f32(W)
     s = q.rtn_scales(Wd, bits)
-    fq = q.fake_quant(Wd, s, bits, dtype=torch.bfloat16)
-    dq = q.dequant(q.pack_to_grid(Wd, s, bits), s, bits, K, N, dtype=torch.bfloat16)
+    fq = _fq(Wd, s, bits, "bf16")
+    g = Guarded((K, N), torch.bfloat16)
+    q.dequant(q.pack_to_grid(Wd, s, bits), s, bits, K, N, out=g.t)
+    dq = g.check("dequant")
     assert torch.equal(fq.view(torch.int16), dq.view(torch.int16))
 
 
@@ -104,7 +115,7 @@ def test_full_size_gate_up():
     K, N = 2560, 19456
     W = workloads.weights(K, N, workloads.seed_for(2, 0, 0))
     sb = quant.rtn_scales(W, 4)
-    got = host_u16(q.fake_quant(dev_f32(W), dev_scales(sb, "f16"), 4, dtype=torch.bfloat16))
+    got = host_u16(_fq(dev_f32(W), dev_scales(sb, "f16"), 4, "bf16"))
     assert np.array_equal(got, quant.fake_quant(W, sb, "f16", 4, "bf16"))
 
 

@@ -6,8 +6,16 @@ and bit-identical across repeated calls (determinism).
 
 Small shapes span several tiles with ragged tails and run every tiling plan
 (columns per wave, K-splitting waves, K-splitting workgroups); the five
-workloads run at full size with the library's own plan, the prefill one on
-sampled outputs.
+workloads run at full size with the library's own plan, every output
+compared (the M = 8192 prefill ones included, with rms over the whole
+output).
+
+Every call writes into a NaN-poisoned output between two canary bands, and
+uses a workspace whose split-K partials / prefill offsets are NaN-poisoned
+and followed by a canary band: an output element a plan leaves unwritten, a
+partial a split never stores, or a store outside either buffer fails the
+test (the caching allocator can no longer hand back a block that still holds
+an earlier plan's correct result).
 """
 
 import numpy as np
@@ -17,7 +25,7 @@ import torch
 import int8_group_quantized_amd as q
 from oracle import gemm, numerics, quant
 import workloads
-from gpu_helpers import dev_bf16, dev_f32, dev_i8, dev_scales, host_u16
+from gpu_helpers import Guarded, GuardedWorkspace, guarded_gemm as _call, dev_bf16, dev_f32, dev_i8, dev_scales, host_u16
 
 pytestmark = pytest.mark.gpu
 
@@ -31,10 +39,12 @@ def _inputs(bits, M, K, N, seed, xstd=1.0):
     return x, c, s
 
 
+
+
 def _run(bits, x, c, s, N, plan=None):
     pg = q.prepack(dev_i8(c), bits)
-    out = q.qgemm(dev_bf16(x), pg, dev_scales(s, SDT[bits]), bits, N, plan=plan)
-    return numerics.bf16_to_f64(host_u16(out))
+    return numerics.bf16_to_f64(_call(dev_bf16(x), pg, dev_scales(s, SDT[bits]), bits, N, plan,
+                                      what="plan %s" % (plan,)))
 
 
 def _assert_close(got, ref, what=""):
@@ -122,8 +132,7 @@ def test_prefill_other_scale_dtype(bits):
     sb = workloads.scales(K // 128, N, other, 7)
     pg = q.prepack(dev_i8(c), bits)
     for m in (M, 1, 16):
-        out = q.qgemm(dev_bf16(x[:m]), pg, dev_scales(sb, other), bits, N)
-        got = numerics.bf16_to_f64(host_u16(out))
+        got = numerics.bf16_to_f64(_call(dev_bf16(x[:m]), pg, dev_scales(sb, other), bits, N))
         _assert_close(got, gemm.gemm_ref(x[:m], c, sb, other), "M=%d" % m)
 
 
@@ -138,8 +147,7 @@ def test_identity_probe_bit_exact(bits, K):
     ref = gemm.gemm_ref(eye, c, s, SDT[bits])
     want = numerics.f64_exact_to_bf16(ref)
     pg = q.prepack(dev_i8(c), bits)
-    out = q.qgemm(dev_bf16(eye), pg, dev_scales(s, SDT[bits]), bits, N)
-    got = host_u16(out)
+    got = _call(dev_bf16(eye), pg, dev_scales(s, SDT[bits]), bits, N)
     bad = np.argwhere(got != want)
     assert bad.size == 0, [(int(k), int(n), int(c[k, n]), hex(got[k, n]), hex(want[k, n]))
                            for k, n in bad[:10]]
@@ -159,24 +167,37 @@ def _zero_code_bound(bits, x, s):
     return 8 * 2.0 ** -24 * 136 * gsum @ np.abs(sv[:, :16])           # [M, 16]
 
 
+ZERO_PLANS = [None, (1, 1, 1), (1, 4, 1), (2, 4, 3), (4, 1, 2), (1, 1, 5)]
+
+
 @pytest.mark.parametrize("bits", [4, 8])
-@pytest.mark.parametrize("M", [1, 5, 200])
+@pytest.mark.parametrize("M", [1, 5, 16, 200])
 def test_zero_codes_scales_and_activations(bits, M):
-    """Zero scales and zero activations give exact zeros on every path; an
-    all-zero code column gives exactly 0 (INT8) or only the rounding of the
-    INT4 offset it cancels."""
+    """Zero scales and zero activations give exact zeros on every path. An
+    all-zero code column gives exactly 0 at M <= 16 on every small-M plan
+    (INT8 codes are exact zeros; INT4 zero codes expand to 136 and cancel
+    against the 136 * sum x offset, which is the same matrix-core chain over
+    the same operands), and at M > 16 exactly 0 for INT8 and only the fp32
+    rounding of the INT4 offset it cancels (the prefill pre-pass seeds the
+    chain with the negated offset)."""
     K, N = 640, 320
     x, c, s = _inputs(bits, M, K, N, 61 + M)
     c[:, :16] = 0                     # first column block: all-zero codes
     s = s.copy()
     s[:, 16:32] = 0                   # second block: zero scales
-    got = _run(bits, x, c, s, N)
-    assert np.all(got[:, 16:32] == 0)
-    assert np.all(np.abs(got[:, :16]) <= _zero_code_bound(bits, x, s))
-    _assert_close(got, gemm.gemm_ref(x, c, s, SDT[bits]))
     z = np.zeros_like(c)
-    assert np.all(np.abs(_run(bits, x, z, s, N)[:, :16]) <= _zero_code_bound(bits, x, s))
-    assert np.all(_run(bits, np.zeros_like(x), c, s, N) == 0)
+    plans = ZERO_PLANS if M <= 16 else [None]
+    for plan in plans:
+        got = _run(bits, x, c, s, N, plan)
+        assert np.all(got[:, 16:32] == 0), plan
+        if M <= 16 or bits == 8:
+            assert np.all(got[:, :16] == 0), plan
+            assert np.all(_run(bits, x, z, s, N, plan) == 0), plan
+        else:
+            assert np.all(np.abs(got[:, :16]) <= _zero_code_bound(bits, x, s))
+            assert np.all(np.abs(_run(bits, x, z, s, N, plan)[:, :16]) <= _zero_code_bound(bits, x, s))
+        _assert_close(got, gemm.gemm_ref(x, c, s, SDT[bits]), "plan %s" % (plan,))
+        assert np.all(_run(bits, np.zeros_like(x), c, s, N, plan) == 0), plan
 
 
 @pytest.mark.parametrize("bits", [4, 8])
@@ -217,8 +238,9 @@ def test_workspace_reuse_across_plans():
     pg = q.prepack(dev_i8(c), 4)
     xd, sd = dev_bf16(x), dev_scales(s, "f16")
     for plan in [(1, 1, 10), (2, 4, 3), (1, 1, 10), (4, 4, 2), (1, 1, 1), (2, 1, 5)]:
-        out = q.qgemm_w4a16(xd, pg, sd, N, plan=plan, ws=ws)
-        _assert_close(numerics.bf16_to_f64(host_u16(out)), ref, str(plan))
+        out = Guarded((M, N), torch.bfloat16)
+        q.qgemm_w4a16(xd, pg, sd, N, out=out.t, plan=plan, ws=ws)
+        _assert_close(numerics.bf16_to_f64(host_u16(out.check(str(plan)))), ref, str(plan))
     assert torch.count_nonzero(ws[:65536]) == 0
 
 
@@ -243,28 +265,16 @@ def test_workloads_full_size(cfg, shape_index):
     sdt = SDT[bits]
     sb = quant.rtn_scales(W, bits)
     codes = quant.q_s(W, numerics.scale_bits_to_f64(sb, sdt), bits)
+    print("workload config %d shape %d: M=%d K=%d N=%d" % (cfg, shape_index, M, K, N), flush=True)
     Wd = dev_f32(W)
     sg = q.rtn_scales(Wd, bits)
     assert np.array_equal(host_u16(sg), sb)
     pg = q.pack_to_grid(Wd, sg, bits)
     del Wd
-    out = q.qgemm(dev_bf16(x), pg, sg, bits, N)
-    got_bits = host_u16(out)
-    if M <= 16:
-        ref = gemm.gemm_ref(x, codes, sb, sdt)
-        _assert_close(numerics.bf16_to_f64(got_bits), ref, "config %d shape %d" % (cfg, shape_index))
-    else:
-        rng = np.random.default_rng(cfg * 7 + shape_index)
-        P = 4096
-        rows = rng.integers(0, M, P)
-        cols = rng.integers(0, N, P)
-        ref = gemm.gemm_ref_at(x, codes, sb, sdt, rows, cols)
-        got = numerics.bf16_to_f64(got_bits[rows, cols])
-        # the rms over the whole output is estimated from the 4096 samples
-        # and taken 10% low, which only tightens the bound
-        ok = gemm.within_tolerance(got, ref, ref_rms=0.9 * gemm.rms(ref))
-        assert ok.all(), (int((~ok).sum()), got[~ok][:5], ref[~ok][:5])
-        assert np.all(np.isfinite(numerics.bf16_to_f64(got_bits)))
+    got_bits = _call(dev_bf16(x), pg, sg, bits, N, what="config %d shape %d" % (cfg, shape_index))
+    # every output, rms over the whole [M, N] output (M = 8192 included)
+    ref = gemm.gemm_ref(x, codes, sb, sdt)
+    _assert_close(numerics.bf16_to_f64(got_bits), ref, "config %d shape %d" % (cfg, shape_index))
 
 
 @pytest.mark.parametrize("bits", [4, 8])
@@ -281,3 +291,54 @@ def test_heavy_tailed_weights_through_rtn(bits, M):
     sv = numerics.scale_bits_to_f64(sb, SDT[bits])
     assert sv.max() / sv[sv > 0].min() > 8        # the scales do spread
     _assert_close(_run(bits, x, c, sb, N), gemm.gemm_ref(x, c, sb, SDT[bits]), "M=%d" % M)
+
+
+def _prefill_walk(M, N):
+    """Host mirror of the prefill plan's tile-width choice and of the
+    condition under which its tile walk goes panel by panel (each XCD's
+    share of tiles is whole tile rows); returns (wn, tiles_n, panel walk,
+    width of the last panel). Used only to document what a case covers."""
+    tiles_m, NB = -(-M // 64), N // 16
+    best, pick = -1.0, None
+    for wn in (4, 2):
+        tn = -(-NB // (4 * wn))
+        tiles = tiles_m * tn
+        slots = 256 * (2 if wn == 4 else 3)
+        eff = tiles / (-(-tiles // slots) * slots) * (1.0 if wn == 4 else 0.85)
+        if eff > best + 1e-9:
+            best, pick = eff, (wn, tn, tiles)
+    wn, tn, tiles = pick
+    per = tiles // 8
+    return wn, tn, per % tn == 0, tn % 8
+
+
+PANEL_CASES = [(4096, 256, 19456), (1024, 384, 2560)]
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("act", ["bf16", "f16"])
+@pytest.mark.parametrize("cbm", [False, True])
+@pytest.mark.parametrize("M,K,N", PANEL_CASES)
+def test_prefill_panel_walk_full_output(bits, act, cbm, M, K, N):
+    """The production prefill tile walk (the one the M = 8192 calls take:
+    64-row tiles dealt to XCDs in whole tile rows, walked in panels of eight
+    column tiles with a narrower last panel), every output compared. The
+    first case uses 64 x 256 tiles (76 tile columns: nine panels of eight and
+    one of four), the second 64 x 128 tiles (20 tile columns: two panels of
+    eight and one of four); with fp16 activations and column-block-major
+    scales as well."""
+    wn, tn, panel, last = _prefill_walk(M, N)
+    assert panel and last, (wn, tn)
+    print("panel walk: bits=%d act=%s cbm=%s M=%d K=%d N=%d wn=%d tiles_n=%d"
+          % (bits, act, cbm, M, K, N, wn, tn), flush=True)
+    x = workloads.activations(M, K, 1300 + M, dtype=act)
+    c = workloads.codes(K, N, bits, 1301 + M)
+    s = workloads.scales(K // 128, N, SDT[bits], 1302 + M)
+    xd = dev_bf16(x) if act == "bf16" else torch.from_numpy(x.view(np.int16)).view(
+        torch.float16).to("cuda:0")
+    sd = dev_scales(s, SDT[bits])
+    if cbm:
+        sd = q.prepack_scales(sd)
+    pg = q.prepack(dev_i8(c), bits)
+    got = numerics.act_to_f64(_call(xd, pg, sd, bits, N, cbm=cbm, what="panel walk"), act)
+    _assert_close(got, gemm.gemm_ref(x, c, s, SDT[bits], x_dtype=act), "panel walk")

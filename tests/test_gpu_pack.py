@@ -1,6 +1,10 @@
 """GPU parity for the integer/byte side of the path: RTN scales, Q_s codes,
 packed bytes, unpack and prepack. The bar is bit-exact against the oracle.
 
+Every output is written into a buffer between canary bands, twice, under two
+different poison bytes (float scales under NaN): both results must agree, so
+no byte is left unwritten, and no store lands outside the buffer.
+
 Cases: small shapes spanning several tiles with ragged tails (N not a
 multiple of the 64- or 256-column spans the kernels use), fp32 and bf16
 weights, crafted ties / clamp ends / zero groups / NaN / infinities /
@@ -15,7 +19,8 @@ import torch
 import int8_group_quantized_amd as q
 from oracle import layout, numerics, quant
 import workloads
-from gpu_helpers import dev_bf16, dev_f32, dev_i8, dev_scales, host_i8, host_u16, host_u8
+from gpu_helpers import (Guarded, dev_bf16, dev_f32, dev_i8, dev_scales, host_i8, host_u16, host_u8,
+                         written_twice)
 
 pytestmark = pytest.mark.gpu
 
@@ -31,6 +36,29 @@ def _weights_for(K, N, seed, wdt, dist="normal"):
     return dev_f32(W), W
 
 
+def _rtn(Wd, bits):
+    K, N = Wd.shape
+    g = Guarded((K // 128, N), torch.float16 if bits == 4 else torch.bfloat16)
+    q.rtn_scales(Wd, bits, out=g.t)
+    return g.check("rtn scales")
+
+
+def _pack(Wd, sd, bits):
+    K, N = Wd.shape
+    return written_twice(lambda o: q.pack_to_grid(Wd, sd, bits, out=o),
+                         (q.packed_bytes(bits, K, N),), torch.uint8, "pack_to_grid")
+
+
+def _unpack(pg, K, N, bits):
+    return written_twice(lambda o: q.unpack(pg, K, N, bits, out=o), (K, N), torch.int8, "unpack")
+
+
+def _prepack(cd, bits):
+    K, N = cd.shape
+    return written_twice(lambda o: q.prepack(cd, bits, out=o), (q.packed_bytes(bits, K, N),),
+                         torch.uint8, "prepack")
+
+
 @pytest.mark.parametrize("bits", [4, 8])
 @pytest.mark.parametrize("K,N", SMALL)
 @pytest.mark.parametrize("wdt", ["f32", "bf16"])
@@ -40,13 +68,13 @@ def test_rtn_pack_unpack_small(bits, K, N, wdt):
     codes = quant.q_s(Wf, numerics.scale_bits_to_f64(sb, SDT[bits]), bits)
     ref_packed = layout.pack(codes, bits)
 
-    sg = q.rtn_scales(Wd, bits)
+    sg = _rtn(Wd, bits)
     assert np.array_equal(host_u16(sg), sb)
-    pg = q.pack_to_grid(Wd, sg, bits)
+    pg = _pack(Wd, sg, bits)
     assert np.array_equal(host_u8(pg), ref_packed)
-    cg = q.unpack(pg, K, N, bits)
+    cg = _unpack(pg, K, N, bits)
     assert np.array_equal(host_i8(cg), codes)
-    assert np.array_equal(host_u8(q.prepack(cg, bits)), ref_packed)
+    assert np.array_equal(host_u8(_prepack(cg, bits)), ref_packed)
 
 
 @pytest.mark.parametrize("bits", [4, 8])
@@ -54,9 +82,9 @@ def test_prepack_full_code_range(bits):
     K, N = 512, 80
     lo, hi = (-8, 7) if bits == 4 else (-128, 127)
     c = workloads.codes(K, N, bits, 5, lo=lo, hi=hi)
-    pg = q.prepack(dev_i8(c), bits)
+    pg = _prepack(dev_i8(c), bits)
     assert np.array_equal(host_u8(pg), layout.pack(c, bits))
-    assert np.array_equal(host_i8(q.unpack(pg, K, N, bits)), c)
+    assert np.array_equal(host_i8(_unpack(pg, K, N, bits)), c)
 
 
 def _crafted(bits):
@@ -83,8 +111,8 @@ def test_pack_crafted_cases(bits):
     K, N = W.shape
     codes = quant.q_s(W, numerics.scale_bits_to_f64(s, SDT[bits]), bits)
     assert codes.min() == quant.RANGE[bits][0]          # the clamp end is exercised
-    pg = q.pack_to_grid(dev_f32(W), dev_scales(s, SDT[bits]), bits)
-    got = host_i8(q.unpack(pg, K, N, bits))
+    pg = _pack(dev_f32(W), dev_scales(s, SDT[bits]), bits)
+    got = host_i8(_unpack(pg, K, N, bits))
     bad = np.argwhere(got != codes)
     assert bad.size == 0, [(int(k), int(n), W[k, n], int(got[k, n]), int(codes[k, n]))
                            for k, n in bad[:10]]
@@ -99,7 +127,7 @@ def test_rtn_crafted(bits):
     W[5, 4] = np.nan
     W[7, 9] = 1e-40
     sb = quant.rtn_scales(W, bits)
-    assert np.array_equal(host_u16(q.rtn_scales(dev_f32(W), bits)), sb)
+    assert np.array_equal(host_u16(_rtn(dev_f32(W), bits)), sb)
 
 
 @pytest.mark.parametrize("bits", [4, 8])
@@ -111,13 +139,13 @@ def test_maximum_extents(bits, K, N):
     Wd, Wf = _weights_for(K, N, 11 + (K >> 7), "f32")
     sb = quant.rtn_scales(Wf, bits)
     codes = quant.q_s(Wf, numerics.scale_bits_to_f64(sb, SDT[bits]), bits)
-    sg = q.rtn_scales(Wd, bits)
+    sg = _rtn(Wd, bits)
     assert np.array_equal(host_u16(sg), sb)
-    pg = q.pack_to_grid(Wd, sg, bits)
+    pg = _pack(Wd, sg, bits)
     assert np.array_equal(host_u8(pg), layout.pack(codes, bits))
-    cg = q.unpack(pg, K, N, bits)
+    cg = _unpack(pg, K, N, bits)
     assert np.array_equal(host_i8(cg), codes)
-    assert torch.equal(q.prepack(cg, bits), pg)
+    assert torch.equal(_prepack(cg, bits), pg)
 
 
 @pytest.mark.parametrize("bits", [4, 8])
@@ -129,9 +157,11 @@ def test_full_size_codes(bits, K, N):
     sb = quant.rtn_scales(W, bits)
     codes = quant.q_s(W, numerics.scale_bits_to_f64(sb, SDT[bits]), bits)
     Wd = dev_f32(W)
-    sg = q.rtn_scales(Wd, bits)
+    sg = _rtn(Wd, bits)
     assert np.array_equal(host_u16(sg), sb)
-    pg = q.pack_to_grid(Wd, sg, bits)
-    assert np.array_equal(host_i8(q.unpack(pg, K, N, bits)), codes)
+    pg = _pack(Wd, sg, bits)
+    assert np.array_equal(host_u8(pg), layout.pack(codes, bits))
+    cg = _unpack(pg, K, N, bits)
+    assert np.array_equal(host_i8(cg), codes)
     # prepack of the GPU's own unpacked codes reproduces its packed bytes
-    assert torch.equal(q.prepack(q.unpack(pg, K, N, bits), bits), pg)
+    assert torch.equal(_prepack(cg, bits), pg)

@@ -1,17 +1,19 @@
 """Column-block-major scales (qg_prepack_scales): the prepacked order equals
-the oracle's element-by-element statement of it, and every GEMM path gives
+the oracle's element-by-element statement of it, every GEMM path gives
 bit-identical outputs with the prepacked scales and with the logical ones
-(the order changes where a scale is read, never the arithmetic), which the
-logical path's own parity tests tie to the oracle."""
+(the order changes where a scale is read, never the arithmetic), and each
+prepacked-scale result also meets the acceptance bound against the oracle's
+float64 product directly. Outputs and workspaces are NaN-poisoned between
+canary bands."""
 
 import numpy as np
 import pytest
 import torch
 
 import int8_group_quantized_amd as q
-from oracle import layout
+from oracle import gemm, layout, numerics
 import workloads
-from gpu_helpers import dev_bf16, dev_i8, dev_scales, host_u16
+from gpu_helpers import Guarded, GuardedWorkspace, dev_bf16, dev_i8, dev_scales, guarded_gemm, host_u16
 
 pytestmark = pytest.mark.gpu
 
@@ -23,7 +25,10 @@ SDT = {4: "f16", 8: "bf16"}
 def test_prepack_matches_oracle(sdt, K, N):
     print("prepack scales: K=%d N=%d %s" % (K, N, sdt), flush=True)
     s = workloads.scales(K // 128, N, sdt, K + N)
-    got = host_u16(q.prepack_scales(dev_scales(s, sdt))).reshape(-1)
+    sd = dev_scales(s, sdt)
+    g = Guarded((N // 16, K // 128, 16), sd.dtype)
+    q.prepack_scales(sd, out=g.t)
+    got = host_u16(g.check("prepack scales")).reshape(-1)
     assert np.array_equal(got, layout.scales_cbm(s))
 
 
@@ -34,9 +39,14 @@ def _pair(bits, M, K, N, seed, plan=None, f16=False):
     pg = q.prepack(dev_i8(c), bits)
     xs = torch.from_numpy(x.view(np.int16)).view(torch.float16 if f16 else torch.bfloat16).cuda()
     sd = dev_scales(s, SDT[bits])
-    ref = q.qgemm(xs, pg, sd, bits, N, plan=plan)
-    got = q.qgemm(xs, pg, q.prepack_scales(sd), bits, N, plan=plan, scales_cbm=True)
-    return host_u16(ref), host_u16(got)
+    ref = guarded_gemm(xs, pg, sd, bits, N, plan=plan, what="logical scales")
+    got = guarded_gemm(xs, pg, q.prepack_scales(sd), bits, N, plan=plan, cbm=True,
+                       what="column-block-major scales")
+    act = "f16" if f16 else "bf16"
+    exact = gemm.gemm_ref(x, c, s, SDT[bits], x_dtype=act)
+    ok = gemm.within_tolerance(numerics.act_to_f64(got, act), exact)
+    assert ok.all(), "%d of %d outside tolerance" % ((~ok).sum(), ok.size)
+    return ref, got
 
 
 @pytest.mark.parametrize("bits", [4, 8])
@@ -68,15 +78,28 @@ def test_fp16_activations_bit_identical(bits, M):
 @pytest.mark.parametrize("M", [16, 40])
 def test_grouped_bit_identical(bits, M):
     K = 1280
-    x = dev_bf16(workloads.activations(M, K, 600 + M))
-    items, items_cbm = [], []
+    xh = workloads.activations(M, K, 600 + M)
+    x = dev_bf16(xh)
+    items, items_cbm, host = [], [], []
     for i, N in enumerate((1024, 512, 3584)):
         c = workloads.codes(K, N, bits, 610 + i)
-        sd = dev_scales(workloads.scales(K // 128, N, SDT[bits], 620 + i), SDT[bits])
+        s = workloads.scales(K // 128, N, SDT[bits], 620 + i)
+        host.append((c, s, N))
+        sd = dev_scales(s, SDT[bits])
         pg = q.prepack(dev_i8(c), bits)
         items.append((pg, sd, N))
         items_cbm.append((pg, q.prepack_scales(sd), N))
-    ref = q.qgemm_grouped(x, items, bits)
-    got = q.qgemm_grouped(x, items_cbm, bits, scales_cbm=True)
-    for r, g in zip(ref, got):
-        assert np.array_equal(host_u16(r), host_u16(g))
+    def run(its, cbm):
+        outs = [Guarded((M, N), torch.bfloat16) for _, _, N in its]
+        ws = GuardedWorkspace(q.grouped_workspace_bytes(bits, M, K, its))
+        q.qgemm_grouped(x, its, bits, outs=[o.t for o in outs], ws=ws.t, scales_cbm=cbm)
+        res = [host_u16(o.check()) for o in outs]
+        ws.check()
+        return res
+
+    ref = run(items, False)
+    got = run(items_cbm, True)
+    for r, g, (c, s, N) in zip(ref, got, host):
+        assert np.array_equal(r, g)
+        ok = gemm.within_tolerance(numerics.bf16_to_f64(g), gemm.gemm_ref(xh, c, s, SDT[bits]))
+        assert ok.all(), (N, int((~ok).sum()))
