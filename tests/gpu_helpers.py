@@ -136,7 +136,7 @@ def written_twice(fn, shape, dtype, what=""):
     return res[0]
 
 
-def guarded_gemm(x_dev, pg, sd, bits, N, plan=None, cbm=False, what=""):
+def guarded_gemm(x_dev, pg, sd, bits, N, *, plan=None, cbm=False, what=""):
     """One GEMM call into a NaN-poisoned output between canary bands, with a
     workspace whose data part is NaN-poisoned and followed by a canary band;
     returns the output's 16-bit patterns on the host after both checks."""

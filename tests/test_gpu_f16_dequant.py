@@ -33,8 +33,8 @@ def _inputs(bits, M, K, N, seed, xstd=1.0):
 
 def _run(bits, x, c, s, N, plan=None):
     pg = q.prepack(dev_i8(c), bits)
-    return numerics.f16_to_f64(_call(dev_f16(x), pg, dev_scales(s, SDT[bits]), bits, N, plan,
-                                     "plan %s" % (plan,)))
+    return numerics.f16_to_f64(_call(dev_f16(x), pg, dev_scales(s, SDT[bits]), bits, N, plan=plan,
+                                     what="plan %s" % (plan,)))
 
 
 def _close(got, ref, what=""):
