@@ -327,6 +327,26 @@ qg_status qg_swa_attention_chunk(const void* q, const void* k_cache, const void*
                                  int64_t window, float scale, int64_t chunk, void* workspace,
                                  size_t workspace_bytes, void* stream);
 
+/* qgemm_w4a16 for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * It takes no workspace argument: the split-K partials, arrival counters
+ * and prefill INT4 offsets go to the library's fixed scratch buffer, a
+ * device array of qg_noalloc_scratch_bytes() (8 MiB) that every GPU the
+ * library runs on holds until the process ends. The call allocates and
+ * frees nothing. Arguments, checks, results and errors are those of
+ * qgemm_w4a16 with the workspace omitted, plus QG_ERR_WORKSPACE when
+ * qg_workspace_bytes(4, M, K, N) exceeds the scratch (e.g. a prefill past
+ * about 27,000 rows at K = 9728), and QG_ERR_HIP when the scratch address
+ * cannot be obtained. The first call on a device also enqueues, on stream,
+ * the clearing of the scratch's arrival counters (every later call leaves
+ * them at zero). All calls on one GPU share that GPU's scratch: calls that
+ * may overlap in time on one GPU (concurrent streams, or graphs replayed
+ * on several streams) race and must be ordered by the caller. */
+size_t qg_noalloc_scratch_bytes(void);
+qg_status qgemm_w4a16_noalloc(const void* x, const void* packed_w, const void* scales,
+                              qg_dtype s_dt, void* out, int64_t M, int64_t K, int64_t N,
+                              void* stream);
+
 /* Column-block-major scales: a storage order of the same scales, prepared
  * once at load time like the packed codes. The logical scales[K/128, N]
  * (group g, column n) become cbm[N/16][K/128][16] with

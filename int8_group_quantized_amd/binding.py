@@ -79,6 +79,8 @@ _SIGNATURES = {
                                                                      _P], _INT),
     "qg_read_stream": ([_P, _SZ, _INT, _P, _P], _INT),
     "qg_prepack_scales": ([_P, _INT, _I64, _I64, _P, _P], _INT),
+    "qg_noalloc_scratch_bytes": ([], _SZ),
+    "qgemm_w4a16_noalloc": ([_P, _P, _P, _INT, _P, _I64, _I64, _I64, _P], _INT),
 }
 
 

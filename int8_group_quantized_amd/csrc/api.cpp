@@ -383,6 +383,23 @@ qg_status qgemm_w8a16(const void* x, const void* packed_w, const void* scales, q
               0, 0, stream);
 }
 
+size_t qg_noalloc_scratch_bytes(void) { return qg::kScratchBytes; }
+
+qg_status qgemm_w4a16_noalloc(const void* x, const void* packed_w, const void* scales,
+                              qg_dtype s_dt, void* out, int64_t M, int64_t K, int64_t N,
+                              void* stream) {
+  // Every check of qgemm_w4a16 first, on the host; then the workspace this
+  // call would need against the fixed scratch (QG_ERR_WORKSPACE beyond it);
+  // only then any HIP call.
+  const qg_status s = gemm_check(x, packed_w, scales, s_dt, out, M, K, N);
+  if (s != QG_OK || M == 0) return s;
+  const size_t need = workspace_bytes(4, M, K, N, 0, 0, 0);
+  if (need > qg::kScratchBytes) return QG_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (need > 0 && qg::scratch_for_stream(as_stream(stream), &ws) != hipSuccess) return QG_ERR_HIP;
+  return gemm(4, false, x, packed_w, scales, s_dt, out, M, K, N, ws, need, 0, 0, 0, stream);
+}
+
 qg_status qgemm_w4a16_plan(const void* x, const void* packed_w, const void* scales, qg_dtype s_dt,
                            void* out, int64_t M, int64_t K, int64_t N, void* workspace,
                            size_t workspace_bytes, int cols_per_wave, int k_waves, int splits,

@@ -116,6 +116,14 @@ hipError_t launch_swa_attention(const SwaPlan& p, const void* q, const void* k, 
                                 int64_t Hkv, int64_t S_max, float scale, void* ws,
                                 hipStream_t st);
 
+// The fixed scratch buffer of the no-allocation entry point (scratch.hip):
+// kScratchBytes of device memory per GPU, held for the life of the process.
+// Returns its device address on the stream's device (taken once per device
+// with hipGetSymbolAddress) and, on that device's first use, enqueues on st
+// the clearing of its arrival counters.
+constexpr size_t kScratchBytes = size_t(8) << 20;
+hipError_t scratch_for_stream(hipStream_t st, void** ptr);
+
 // Read-stream probe (read_probe.hip): reads bytes (a multiple of 16) at src
 // once over `workgroups` workgroups of 256 threads; stores kReadProbeMark to
 // sink only when a thread's XOR of what it read equals it.

@@ -267,3 +267,22 @@ def test_prepacked_scales_only_for_gemms(cbm):
     assert L.qg_fake_quant_w4(FAKE, 2, FAKE, cbm, 128, 16, FAKE, 0, None) == DTYPE
     assert _gemm(M=1, K=100, N=512, sdt=cbm) == SHAPE          # accepted dtype, shape checked
     assert L.qgemm_w4a16(FAKE, FAKE, FAKE, 5, FAKE, 1, 256, 512, 0, 0, None) == DTYPE
+
+
+def test_noalloc_gemm_validates_before_any_device_call():
+    """The no-allocation W4A16 GEMM: the checks of qgemm_w4a16, then the
+    workspace the call would need against the fixed scratch, all on the
+    host (these calls reach no device)."""
+    L = q.lib()
+    assert L.qg_noalloc_scratch_bytes() == 8 << 20
+    f = L.qgemm_w4a16_noalloc
+    assert f(FAKE, FAKE, FAKE, 1, FAKE, 1, 100, 512, None) == SHAPE
+    assert f(FAKE, FAKE, FAKE, 1, FAKE, 1, 256, 24, None) == SHAPE
+    assert f(0, FAKE, FAKE, 1, FAKE, 1, 256, 512, None) == NULL
+    assert f(FAKE, FAKE, 0, 1, FAKE, 1, 256, 512, None) == NULL
+    assert f(MIS, FAKE, FAKE, 1, FAKE, 1, 256, 512, None) == ALIGN
+    assert f(FAKE, FAKE, FAKE, 2, FAKE, 1, 256, 512, None) == DTYPE
+    assert f(0, FAKE, FAKE, 1, 0, 0, 256, 512, None) == OK          # M = 0: nothing to do
+    # a prefill whose INT4 offsets (30016 rows x 76 groups x 4 B) exceed 8 MiB
+    assert L.qg_workspace_bytes(4, 30000, 9728, 16) > L.qg_noalloc_scratch_bytes()
+    assert f(FAKE, FAKE, FAKE, 1, FAKE, 30000, 9728, 16, None) == WS
