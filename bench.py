@@ -72,9 +72,9 @@ def parse():
     return ap.parse_args()
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_small_w4a16_gate_up_m1.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemv_w4a16_gate_up_m1.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "int8_group_quantized_amd", "csrc", f)
-                  for f in ("gemm_small.hip", "qg_device.h")]
+                  for f in ("gemv.hip", "qg_device.h")]
 
 
 def kernel_source_hash():
@@ -682,7 +682,7 @@ def main():
     c_gbs, b_gbs = c_bytes / c_us / 1e3, b_bytes / b_us / 1e3
     roofline = {"bound": "hbm", "achieved": round(k_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(k_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
-                "kernel": "gemm_small_kernel<4,...> gate/up K=2560 N=19456 M=1",
+                "kernel": "gemv_kernel<4,...> gate/up K=2560 N=19456 M=1",
                 "us_per_launch": round(k_ms * 1e3, 3), "bytes_per_launch": up.bytes,
                 "read_stream_ceiling": {
                     "probe": "qg_read_stream, 16-byte nontemporal loads, fastest of "
