@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libqgemm.so")
 SOURCES = ["api.cpp", "pack_kernels.hip", "gemm_small.hip", "gemm_prefill.hip",
-           "swa_attention.hip", "read_probe.hip", "scratch.hip", "gemv.hip"]
+           "swa_attention.hip", "read_probe.hip", "scratch.hip", "gemv.hip", "plans.cpp"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

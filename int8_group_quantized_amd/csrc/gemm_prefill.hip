@@ -33,7 +33,7 @@
 namespace qg {
 namespace {
 
-constexpr int kBM = 64;                      // rows per workgroup tile
+constexpr int kBM = kPrefillRows;            // rows per workgroup tile
 constexpr int kXcds = 8;
 constexpr int kPanel = 8;                    // column tiles per panel of the tile walk
 constexpr int kXBytes = kBM * kGroup * 2;    // one group of x for the tile: 16 KiB
@@ -314,41 +314,7 @@ void launch_bits(const PrefillPlan& p, const uint16_t* x, const char* w, const u
   else           launch_main<BITS, SBF, XH, 2, 2>(p, x, w, s, nb, out, M, K, N, scbm, st);
 }
 
-constexpr int kCUs = 256;   // MI355X compute units (plan heuristic only)
-
 }  // namespace
-
-// Tile width: 256 columns (four wavefronts, two workgroups per CU) unless
-// 128 columns (two wavefronts, three per CU) fills the last round of
-// workgroups better.
-bool make_prefill_plan(int64_t M, int64_t K, int64_t N, PrefillPlan* plan) {
-  const int64_t tiles_m = (M + kBM - 1) / kBM;
-  const int64_t NB = N / kTileCols;
-  double best = -1.0;
-  for (int wn : {4, 2}) {
-    const int64_t tiles = tiles_m * ((NB + 4 * wn - 1) / (4 * wn));
-    const int64_t slots = (int64_t)kCUs * (wn == 4 ? 2 : 3);
-    const int64_t rounds = (tiles + slots - 1) / slots;
-    // useful fraction of the occupied slot-rounds, with the narrower tile's
-    // extra x traffic priced at 15%
-    const double eff = (double)tiles / (double)(rounds * slots) * (wn == 4 ? 1.0 : 0.85);
-    if (tiles > 0x7FFFFFFF) return false;
-    if (eff > best + 1e-9) {
-      best = eff;
-      plan->wn = wn;
-      plan->tiles_n = (int)((NB + 4 * wn - 1) / (4 * wn));
-      plan->tiles = (int)tiles;
-    }
-  }
-  plan->mp = tiles_m * kBM;
-  if (plan->mp * (K / kGroup) > 0x7FFFFFFF) return false;
-  return true;
-}
-
-size_t prefill_workspace(int bits, const PrefillPlan& p, int64_t K) {
-  if (bits != 4) return 0;
-  return (size_t)kCounterBytes + (size_t)p.mp * (size_t)(K / kGroup) * sizeof(float);
-}
 
 hipError_t launch_gemm_prefill(int bits, const PrefillPlan& p, const void* x, bool x_f16,
                                const void* packed, const void* scales, bool s_bf16, bool s_cbm,

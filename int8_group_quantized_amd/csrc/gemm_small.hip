@@ -52,9 +52,6 @@
 namespace qg {
 namespace {
 
-constexpr int kMaxCounters = kCounterBytes / sizeof(uint32_t);
-constexpr int64_t kLdsAuto = 80 * 1024;     // LDS per workgroup the library's own plans use
-constexpr int64_t kLdsMax = 160 * 1024;     // LDS a workgroup may have (explicit plans)
 
 // Device-coherent (agent scope) accesses for the split-K partials.
 __device__ __forceinline__ void store_coherent(float* p, float v) {
@@ -516,110 +513,7 @@ hipError_t launch_shape(const SmallPlan& p, const void* x, const GroupArgs& g, b
   return hipErrorInvalidValue;
 }
 
-bool shape_supported(int nbw, int wn, int wk) {
-  static const int ok[][3] = {{1, 4, 1}, {1, 2, 2}, {1, 1, 4}, {1, 1, 8},
-                              {2, 4, 1}, {2, 1, 4}, {4, 4, 1}, {4, 1, 4}};
-  for (const auto& s : ok)
-    if (s[0] == nbw && s[1] == wn && s[2] == wk) return true;
-  return false;
-}
-
-// LDS bytes per staged group: x fragments (rows padded to 16 unless M == 1)
-// and the 16 scales of each of the workgroup's column blocks.
-int64_t lds_per_group(int wn, int nbw, int mr) {
-  return (mr == 1 ? 256 : 4096) + (int64_t)wn * nbw * 32;
-}
-
 }  // namespace
-
-size_t small_plan_lds_bytes(const SmallPlan& p, int64_t M) {
-  (void)M;
-  const size_t stage = (size_t)p.sg * (size_t)lds_per_group(p.wn, p.nbw, p.mr) + 256;
-  const size_t red = (size_t)(p.wk - 1) * p.wn * p.nbw * 64 * 16;
-  return stage > red ? stage : red;
-}
-
-bool make_small_plan(int bits, int64_t M, int64_t K, int64_t N, int nbw, int wk, int splits,
-                     SmallPlan* plan) {
-  const int64_t NB = N / kTileCols;
-  const int64_t G = K / kGroup;
-  SmallPlan p;
-  p.bits = bits;
-  p.mr = (M == 1) ? 1 : 16;
-  p.row_blocks = (int)((M + 15) / 16);
-  const bool own = (nbw == 0 && wk == 0 && splits == 0);
-  if (own) {
-    // The library's own plan, from sweeps of the decode and verification
-    // shapes on MI355X: four wavefronts splitting K for one row, each with
-    // two column blocks when N is wide (the offset chain and the x reads
-    // serve both) and one otherwise; for 2-16 rows, wide N shares each
-    // staged x group between eight column blocks (two per wavefront), long K
-    // splits across workgroups of four column blocks (about 16 INT4 or 13
-    // INT8 groups each), and the rest use four K-wavefronts per column block.
-    if (M == 1) {
-      nbw = NB >= 1024 ? 2 : 1; wk = 4;
-    } else if (NB >= 1024) {
-      nbw = 2; wk = 1; splits = 1;
-    } else if (G >= 40) {
-      const int per = bits == 4 ? 16 : 13;
-      nbw = 1; wk = 1; splits = (int)((G + per - 1) / per);
-    } else {
-      nbw = 1; wk = 4;
-    }
-  }
-  if (nbw == 0) nbw = 1;
-  if (wk == 0) {
-    // Enough column-block waves to fill the chip without splitting K, else
-    // waves that split K inside a workgroup.
-    wk = (NB >= 1024) ? 1 : (NB >= 128 ? 4 : 8);
-  }
-  const int wn = (wk >= 8) ? 1 : ((nbw >= 2 && wk == 4) ? 1 : 4 / wk);
-  if (!shape_supported(nbw, wn, wk)) return false;
-  p.nbw = nbw;
-  p.wk = wk;
-  p.wn = wn;
-  p.wgs_n = (int)((NB + (int64_t)wn * nbw - 1) / ((int64_t)wn * nbw));
-  // The workgroup stages x and the scales for its whole K range at once.
-  // The library's plans split K across workgroups so that this fits two
-  // workgroups per CU; explicit plans may use up to a CU's LDS.
-  const int64_t per_group = lds_per_group(wn, nbw, p.mr);
-  if (splits == 0) {
-    // The own plan may use up to a CU's LDS; other plans keep two
-    // workgroups per CU.
-    const int64_t fit = ((own ? kLdsMax - 512 : kLdsAuto - 256)) / per_group;
-    splits = (int)((G + fit - 1) / fit);
-  } else if (own) {
-    const int64_t fit = (kLdsMax - 512) / per_group;
-    splits = (int)std::max<int64_t>(splits, (G + fit - 1) / fit);
-  }
-  if (splits < 1 || splits > G) return false;
-  p.gps = (int)((G + splits - 1) / splits);
-  p.splits = (int)((G + p.gps - 1) / p.gps);   // no empty split
-  p.sg = p.gps;
-  if (p.splits > 65535 || p.row_blocks > 65535) return false;
-  if (p.splits > 1 && (int64_t)p.wgs_n * p.row_blocks > kMaxCounters) return false;
-  if ((int64_t)small_plan_lds_bytes(p, M) > kLdsMax) return false;
-  *plan = p;
-  return true;
-}
-
-size_t small_plan_workspace(const SmallPlan& p, int64_t M, int64_t N) {
-  if (p.splits <= 1) return 0;
-  return (size_t)kCounterBytes + (size_t)p.splits * (size_t)M * (size_t)N * sizeof(float);
-}
-
-void small_plan_group(const SmallPlan& p, GroupArgs* g) {
-  const int per = p.wn * p.nbw;                      // column blocks per workgroup
-  int wg = 0, col = 0;
-  for (int i = 0; i < g->count; ++i) {
-    g->item[i].wg_first = wg;
-    g->item[i].col_first = col;
-    wg += (g->item[i].n / kTileCols + per - 1) / per;
-    col += g->item[i].n;
-  }
-  g->wg_total = wg;
-  g->n_total = col;
-}
 
 hipError_t launch_gemm_small(int bits, const SmallPlan& p, const void* x, bool x_f16,
                              const GroupArgs& g, bool s_bf16, bool s_cbm, int64_t M, int64_t K,

@@ -33,7 +33,7 @@
 namespace qg {
 namespace {
 
-constexpr int kGW = 5;   // groups per wavefront per round
+constexpr int kGW = kGemvGroups;   // groups per wavefront per round
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t gemv_rsrc(const void* base, int bytes) {
   // Raw buffer resource: loads at or past `bytes` return zeros, no access.
@@ -166,27 +166,6 @@ hipError_t launch_gr(int wk, const void* x, const GroupArgs& g, bool s_cbm, int6
 }
 
 }  // namespace
-
-int gemv_k_waves(int64_t K) {
-  // Enough wavefronts that each takes about kGW groups (the decode shapes:
-  // K = 2560 -> 4, K = 9728 -> 16), rounded up to a power of two, at most 16.
-  const int64_t want = (K / kGroup + kGW - 1) / kGW;
-  int wk = 1;
-  while (wk < want && wk < 16) wk *= 2;
-  return wk;
-}
-
-void gemv_group(GroupArgs* g) {
-  int wg = 0, col = 0;
-  for (int i = 0; i < g->count; ++i) {
-    g->item[i].wg_first = wg;
-    g->item[i].col_first = col;
-    wg += g->item[i].n / kTileCols;
-    col += g->item[i].n;
-  }
-  g->wg_total = wg;
-  g->n_total = col;
-}
 
 hipError_t launch_gemv(int bits, const void* x, bool x_f16, const GroupArgs& g, bool s_bf16,
                        bool s_cbm, int64_t K, hipStream_t st) {

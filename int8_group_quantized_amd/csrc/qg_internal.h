@@ -10,6 +10,14 @@
 
 namespace qg {
 
+constexpr int kGroup = 128;                 // K extent of one scale group
+constexpr int kTileCols = 16;               // output columns per packed tile
+constexpr uint32_t kCounterBytes = 65536;   // arrival counters at a workspace's start
+constexpr int kPrefillRows = 64;            // rows of a prefill tile
+constexpr int kGemvGroups = 5;              // groups per decode-GEMV wavefront per round
+constexpr int kSwaMaxChunks = 256;          // key chunks one (sequence, head) may have
+constexpr int kSwaPartFloats = 16 * 128 + 32;   // a chunk's record: O[16][128], max[16], sum[16]
+
 // Small-M tiling: each wavefront covers `nbw` 16-column blocks; `wk`
 // wavefronts of a 4-wave workgroup split the K range of the workgroup;
 // `splits` workgroups split K across the grid (fp32 partials + a last-arrival

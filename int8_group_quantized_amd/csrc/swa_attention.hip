@@ -51,8 +51,9 @@ constexpr int kVStageBytes = 32 * kVRowBytes;      // one step: 32 value rows
 constexpr int kWaves = 4;
 constexpr int kWavesLds = kWaves * kVStageBytes;
 constexpr int kOFloats = 16 * kD;                  // one chunk's O[16][128]
-constexpr int kPartFloats = kOFloats + 32;         // + max[16], sum[16]
-constexpr int kMaxChunks = 256;   // merge table of maxima and sums in LDS (128 B per chunk)
+constexpr int kPartFloats = kSwaPartFloats;       // O[16][128], then max[16], sum[16]
+static_assert(kPartFloats == kOFloats + 32, "chunk record layout");
+constexpr int kMaxChunks = kSwaMaxChunks;   // merge table of maxima and sums in LDS (128 B per chunk)
 static_assert(kMaxChunks * 128 <= kWavesLds, "merge table exceeds the LDS stage area");
 static_assert(kMaxChunks * 8 % (64 * kWaves) == 0, "merge table loads");
 constexpr int kCoherent = 16;                  // sc1: bypass the per-XCD L2
@@ -385,37 +386,6 @@ __global__ __launch_bounds__(256, 2) void swa_attention_kernel(
 }
 
 }  // namespace
-
-bool make_swa_plan(int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t S_max, int64_t window,
-                   int64_t chunk_req, SwaPlan* p) {
-  const int64_t w = window >= S_max ? 0 : window;   // a window past every sequence is no window
-  // Longest key span of any sequence: the whole cache without a window; else
-  // a sequence within the window (full attention, at most W keys) or the
-  // block plus W / 2 keys before its first query.
-  const int64_t span = w == 0 ? S_max : std::min<int64_t>(S_max, std::max<int64_t>(w, T + w / 2));
-  // About 384 workgroups over the whole call (a sweep of chunk sizes over the
-  // drafter's Long-context shapes at batch 1 and 8), and at least 256 keys
-  // (two 32-key steps per wavefront) per chunk: a cross-workgroup merge costs
-  // more than a short chunk saves.
-  const int64_t heads = std::max<int64_t>(1, B * Hq);
-  const int64_t target = std::max<int64_t>(1, std::min<int64_t>(64, (384 + heads - 1) / heads));
-  int64_t chunk = (span + target - 1) / target;
-  chunk = std::max<int64_t>(256, (chunk + 31) / 32 * 32);
-  if (chunk_req > 0) chunk = chunk_req;
-  p->window = (int)w;
-  p->chunk = (int)chunk;
-  p->nchunks = (int)((span + chunk - 1) / chunk);
-  const int64_t units = B * Hkv * p->nchunks;
-  p->units = (int)units;
-  if (p->nchunks > kMaxChunks) return false;
-  p->grid = (int)(8 * (Hq / Hkv) * ((units + 7) / 8));
-  return units < (1 << 24);
-}
-
-size_t swa_workspace(const SwaPlan& p, int64_t B, int64_t Hq) {
-  if (p.nchunks <= 1) return 0;
-  return (size_t)kCounterBytes + (size_t)B * Hq * p.nchunks * kPartFloats * sizeof(float);
-}
 
 hipError_t launch_swa_attention(const SwaPlan& p, const void* q, const void* k, const void* v,
                                 const int32_t* seq_lens, void* out, int64_t T, int64_t Hq,

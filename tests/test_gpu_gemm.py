@@ -342,3 +342,19 @@ def test_prefill_panel_walk_full_output(bits, act, cbm, M, K, N):
     pg = q.prepack(dev_i8(c), bits)
     got = numerics.act_to_f64(_call(xd, pg, sd, bits, N, cbm=cbm, what="panel walk"), act)
     _assert_close(got, gemm.gemm_ref(x, c, s, SDT[bits], x_dtype=act), "panel walk")
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("K,N", [(128, 16), (384, 48), (896, 592), (2688, 1040), (10368, 48),
+                                 (10624, 208), (20608, 16)])
+def test_decode_gemv_k_waves_and_rounds(bits, K, N):
+    """M = 1, the decode GEMV: K of 1, 3, 7, 21, 81, 83 and 161 groups, so the
+    number of K-wavefronts runs 1, 1, 2, 8, 16, 16, 16 with ragged (or
+    empty) last wavefronts and one, two or three rounds of five groups per
+    wavefront; the first column block has all-zero codes and must come out
+    exactly 0."""
+    x, c, s = _inputs(bits, 1, K, N, 1700 + K + N)
+    c[:, :16] = 0
+    got = _run(bits, x, c, s, N)
+    assert np.all(got[:, :16] == 0)
+    _assert_close(got, gemm.gemm_ref(x, c, s, SDT[bits]), "K=%d N=%d" % (K, N))
