@@ -104,7 +104,7 @@ qg_status gemm(int bits, bool x_f16, const void* x, const void* packed, const vo
   qg_status s = gemm_check(x, packed, scales, s_dt, out, M, K, N);
   if (s != QG_OK || M == 0) return s;
   const bool explicit_plan = (nbw != 0 || wk != 0 || splits != 0);
-  if (M == 1 && !explicit_plan) {   // decode GEMV: no workspace
+  if (!explicit_plan && (M == 1 || qg::gemv_rows_fits(M, K, N))) {   // GEMV: no workspace
     qg::GroupArgs g;
     g.count = 1;
     g.item[0].n = (int)N;
@@ -112,7 +112,7 @@ qg_status gemm(int bits, bool x_f16, const void* x, const void* packed, const vo
     g.item[0].scales = static_cast<const uint16_t*>(scales);
     g.item[0].out = static_cast<uint16_t*>(out);
     qg::gemv_group(&g);
-    return from_hip(qg::launch_gemv(bits, x, x_f16, g, s_bf16(s_dt), s_cbm(s_dt), K,
+    return from_hip(qg::launch_gemv(bits, x, x_f16, g, s_bf16(s_dt), s_cbm(s_dt), M, K,
                                     as_stream(stream)));
   }
   if (M > kSmallMaxM && !explicit_plan) {
@@ -163,7 +163,7 @@ qg_status grouped_plan(int bits, int64_t M, int64_t K, const qg_group_item* item
   if (s != QG_OK) return s;
   if (M > kSmallMaxM) return QG_OK;
   if (M == 0) return QG_OK;
-  if (M == 1) {   // decode GEMV: one workgroup per column block of every item
+  if (M == 1 || qg::gemv_rows_fits(M, K, ntot)) {   // GEMV: one workgroup per column block
     g->count = count;
     for (int i = 0; i < count; ++i) {
       g->item[i].n = (int)items[i].N;
@@ -192,7 +192,8 @@ size_t grouped_workspace(int bits, int64_t M, int64_t K, const qg_group_item* it
   if (bits != 4 && bits != 8) return 0;
   qg::SmallPlan plan;
   qg::GroupArgs g;
-  if (grouped_plan(bits, M, K, items, count, &plan, &g) != QG_OK || M <= 1) return 0;
+  if (grouped_plan(bits, M, K, items, count, &plan, &g) != QG_OK || M == 0) return 0;
+  if (M == 1 || qg::gemv_rows_fits(M, K, g.n_total)) return 0;
   if (M > kSmallMaxM) {
     qg::PrefillPlan pp;
     if (!qg::make_prefill_plan(M, K, items[0].N, &pp)) return 0;
@@ -232,8 +233,8 @@ qg_status gemm_grouped(int bits, bool x_f16, const void* x, const qg_group_item*
     }
     return QG_OK;
   }
-  if (M == 1)
-    return from_hip(qg::launch_gemv(bits, x, x_f16, g, s_bf16(s_dt), s_cbm(s_dt), K,
+  if (M == 1 || qg::gemv_rows_fits(M, K, g.n_total))
+    return from_hip(qg::launch_gemv(bits, x, x_f16, g, s_bf16(s_dt), s_cbm(s_dt), M, K,
                                     as_stream(stream)));
   return from_hip(qg::launch_gemm_small(bits, plan, x, x_f16, g, s_bf16(s_dt), s_cbm(s_dt), M, K, ws,
                                         as_stream(stream)));
@@ -266,7 +267,7 @@ qg_status fake_quant(int bits, const void* W, qg_dtype w_dt, const void* scales,
 size_t workspace_bytes(int bits, int64_t M, int64_t K, int64_t N, int nbw, int wk, int splits) {
   if ((bits != 4 && bits != 8) || check_mkn(M, K, N) != QG_OK || M == 0) return 0;
   const bool own = nbw == 0 && wk == 0 && splits == 0;
-  if (M == 1 && own) return 0;                                  // decode GEMV
+  if (own && (M == 1 || qg::gemv_rows_fits(M, K, N))) return 0;   // GEMV
   if (M > kSmallMaxM && own) {                                  // prefill kernel
     qg::PrefillPlan pp;
     if (!qg::make_prefill_plan(M, K, N, &pp)) return 0;

@@ -1,4 +1,5 @@
-// Decode GEMV (M = 1) of the group-quantized GEMM:
+// Decode GEMV (M = 1) of the group-quantized GEMM, and its 2-16-row form for
+// narrow verification shapes:
 //   out[n] = bf16( sum_g s[g, n] * sum_{k in g} x[k] * q[k, n] )
 // (arXiv 2607.04244, QAD paragraph: the served weight is s (.) W_q; group of
 // 128 along K per the drafter-PTQ paragraph; INT8 variant per the W8A16
@@ -139,39 +140,163 @@ __global__ __launch_bounds__(64 * WK) void gemv_kernel(const uint16_t* __restric
   if (lq == 0) it.out[cb * 16 + l16] = A::out(acc);
 }
 
+// The same structure for 2-16 rows (a verification block), where the shape
+// is narrow (at most 512 column blocks, at most 40 groups): every 16-row A
+// operand is fully used, so x of a group is four 16-byte loads per lane
+// (rows past M read as zeros), the four K steps chain into one product, and
+// the INT4 offset is the same chain with the constant 136 (exact cancellation
+// for all-zero code columns). x is re-read from L2 by every column block;
+// that costs less than staging it behind a barrier while the column blocks
+// are few (wide shapes use the staged small-M kernel).
+template <int BITS, bool SBF, bool XH, bool GR, int WK>
+__global__ __launch_bounds__(64 * WK) void gemv_rows_kernel(const uint16_t* __restrict__ x, int M,
+                                                            int K, int rounds, int scbm,
+                                                            const GroupArgs ga) {
+  using A = Act<XH>;
+  constexpr int TB = (BITS == 4) ? 1024 : 2048;
+  constexpr int TW = TB / 1024;
+  constexpr int aux = (BITS == 4) ? 2 : 0;
+  __shared__ f32x4 red[WK > 1 ? (WK - 1) * 64 : 1];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l16 = lane & 15, lq = lane >> 4;
+
+  int b = blockIdx.x;
+  const int nwg = gridDim.x;
+  const int b8 = nwg / 8 * 8;
+  if (b < b8) b = (b % 8) * (nwg / 8) + b / 8;
+  int item = 0;
+  if constexpr (GR) {
+    for (int i = 1; i < ga.count; ++i)
+      if (b >= ga.item[i].wg_first) item = i;
+  }
+  const GroupItem& it = ga.item[item];
+  const int N = it.n;
+  const int cb = b - (GR ? it.wg_first : 0);
+  const int G = K >> 7;
+  const uint32_t magic = gemv_opaque(A::kMagic);
+  const u32x4 off = {A::kOffset, A::kOffset, A::kOffset, A::kOffset};
+  // A operand: lane (row l16, K slice lq); rows >= M lie past the resource
+  // (M rows of K values) and read as zeros.
+  const __amdgpu_buffer_rsrc_t xr = gemv_rsrc(x, M * K * 2);
+  const int xrow = l16 * K * 2 + 16 * lq;
+
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int r = 0; r < rounds; ++r) {
+    const int g0 = min((r * WK + wave) * kGW, G);
+    const int wn = min(kGW, G - g0);
+    if (wn <= 0) break;
+    const __amdgpu_buffer_rsrc_t tr = gemv_rsrc(it.packed + ((int64_t)cb * G + g0) * TB, wn * TB);
+    const __amdgpu_buffer_rsrc_t sr =
+        scbm ? gemv_rsrc(it.scales + ((int64_t)cb * G + g0) * 16, wn * 32)
+             : gemv_rsrc(it.scales + (int64_t)g0 * N + cb * 16, ((wn - 1) * N + 16) * 2);
+    const int sstride = scbm ? 16 : N;
+
+    u32x4 xa[kGW][4];
+    u32x4 t[kGW][TW];
+    uint32_t sb[kGW];
+#pragma unroll
+    for (int d = 0; d < kGW; ++d) {
+      // groups past this wavefront's last read x as zeros too
+      const int xo = (d < wn) ? xrow + (g0 + d) * kGroup * 2 : 0x7FFFFFF0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        xa[d][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 xr, (d < wn) ? xo + 64 * j : xo, 0, 0));
+      sb[d] = __builtin_amdgcn_raw_buffer_load_b16(sr, (d * sstride + l16) * 2, 0, 0);
+#pragma unroll
+      for (int v = 0; v < TW; ++v)
+        t[d][v] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(tr, lane * (TB / 64) + d * TB + 16 * v, 0, aux));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int d = 0; d < kGW; ++d) {
+      f32x4 p = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (BITS == 4) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) p = A::mma(xa[d][j], int4_word_to_act(t[d][0][j], magic), p);
+        f32x4 bias = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bias = A::mma(xa[d][j], off, bias);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p[e] -= bias[e];
+      } else {
+        p = A::mma(xa[d][0], int8_words_to_act<A>(t[d][0][0], t[d][0][1]), p);
+        p = A::mma(xa[d][1], int8_words_to_act<A>(t[d][0][2], t[d][0][3]), p);
+        p = A::mma(xa[d][2], int8_words_to_act<A>(t[d][1][0], t[d][1][1]), p);
+        p = A::mma(xa[d][3], int8_words_to_act<A>(t[d][1][2], t[d][1][3]), p);
+      }
+      const float sv = d < wn ? scale_to_f32(sb[d], SBF) : 0.0f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = fmaf(sv, p[e], acc[e]);
+    }
+  }
+
+  if constexpr (WK > 1) {
+    if (wave > 0) red[(wave - 1) * 64 + lane] = acc;
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int w = 0; w < WK - 1; ++w) {
+      const f32x4 o = red[w * 64 + lane];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] += o[e];
+    }
+  }
+  // C layout: lane holds column l16, rows 4 lq + e
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int row = 4 * lq + e;
+    if (row < M) it.out[(int64_t)row * N + cb * 16 + l16] = A::out(acc[e]);
+  }
+}
+
 template <int BITS, bool SBF, bool XH, bool GR>
-hipError_t launch_wk(int wk, const void* x, const GroupArgs& g, bool s_cbm, int64_t K,
+hipError_t launch_wk(int wk, const void* x, const GroupArgs& g, bool s_cbm, int64_t M, int64_t K,
                      hipStream_t st) {
   const int G = (int)(K / kGroup);
   const int rounds = (G + wk * kGW - 1) / (wk * kGW);
   const auto* xp = static_cast<const uint16_t*>(x);
   const int scbm = s_cbm ? 1 : 0;
+  const int m = (int)M, k = (int)K;
   const dim3 grid((unsigned)g.wg_total);
-  switch (wk) {
-    case 1: gemv_kernel<BITS, SBF, XH, GR, 1><<<grid, 64, 0, st>>>(xp, (int)K, rounds, scbm, g); break;
-    case 2: gemv_kernel<BITS, SBF, XH, GR, 2><<<grid, 128, 0, st>>>(xp, (int)K, rounds, scbm, g); break;
-    case 4: gemv_kernel<BITS, SBF, XH, GR, 4><<<grid, 256, 0, st>>>(xp, (int)K, rounds, scbm, g); break;
-    case 8: gemv_kernel<BITS, SBF, XH, GR, 8><<<grid, 512, 0, st>>>(xp, (int)K, rounds, scbm, g); break;
-    case 16: gemv_kernel<BITS, SBF, XH, GR, 16><<<grid, 1024, 0, st>>>(xp, (int)K, rounds, scbm, g); break;
-    default: return hipErrorInvalidValue;
+  if (M == 1) {
+    switch (wk) {
+      case 1: gemv_kernel<BITS, SBF, XH, GR, 1><<<grid, 64, 0, st>>>(xp, k, rounds, scbm, g); break;
+      case 2: gemv_kernel<BITS, SBF, XH, GR, 2><<<grid, 128, 0, st>>>(xp, k, rounds, scbm, g); break;
+      case 4: gemv_kernel<BITS, SBF, XH, GR, 4><<<grid, 256, 0, st>>>(xp, k, rounds, scbm, g); break;
+      case 8: gemv_kernel<BITS, SBF, XH, GR, 8><<<grid, 512, 0, st>>>(xp, k, rounds, scbm, g); break;
+      case 16: gemv_kernel<BITS, SBF, XH, GR, 16><<<grid, 1024, 0, st>>>(xp, k, rounds, scbm, g); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (wk) {
+      case 1: gemv_rows_kernel<BITS, SBF, XH, GR, 1><<<grid, 64, 0, st>>>(xp, m, k, rounds, scbm, g); break;
+      case 2: gemv_rows_kernel<BITS, SBF, XH, GR, 2><<<grid, 128, 0, st>>>(xp, m, k, rounds, scbm, g); break;
+      case 4: gemv_rows_kernel<BITS, SBF, XH, GR, 4><<<grid, 256, 0, st>>>(xp, m, k, rounds, scbm, g); break;
+      case 8: gemv_rows_kernel<BITS, SBF, XH, GR, 8><<<grid, 512, 0, st>>>(xp, m, k, rounds, scbm, g); break;
+      default: return hipErrorInvalidValue;
+    }
   }
   return hipGetLastError();
 }
 
 template <int BITS, bool SBF, bool XH>
-hipError_t launch_gr(int wk, const void* x, const GroupArgs& g, bool s_cbm, int64_t K,
+hipError_t launch_gr(int wk, const void* x, const GroupArgs& g, bool s_cbm, int64_t M, int64_t K,
                      hipStream_t st) {
-  return g.count > 1 ? launch_wk<BITS, SBF, XH, true>(wk, x, g, s_cbm, K, st)
-                     : launch_wk<BITS, SBF, XH, false>(wk, x, g, s_cbm, K, st);
+  return g.count > 1 ? launch_wk<BITS, SBF, XH, true>(wk, x, g, s_cbm, M, K, st)
+                     : launch_wk<BITS, SBF, XH, false>(wk, x, g, s_cbm, M, K, st);
 }
 
 }  // namespace
 
 hipError_t launch_gemv(int bits, const void* x, bool x_f16, const GroupArgs& g, bool s_bf16,
-                       bool s_cbm, int64_t K, hipStream_t st) {
+                       bool s_cbm, int64_t M, int64_t K, hipStream_t st) {
   const int wk = gemv_k_waves(K);
+  if (M < 1 || M > 16 || (M > 1 && wk > 8)) return hipErrorInvalidValue;
 #define QG_GV(B, S, H) \
-  if (bits == B && s_bf16 == S && x_f16 == H) return launch_gr<B, S, H>(wk, x, g, s_cbm, K, st);
+  if (bits == B && s_bf16 == S && x_f16 == H) return launch_gr<B, S, H>(wk, x, g, s_cbm, M, K, st);
   QG_GV(4, false, false) QG_GV(4, true, false) QG_GV(8, false, false) QG_GV(8, true, false)
   QG_GV(4, false, true) QG_GV(4, true, true) QG_GV(8, false, true) QG_GV(8, true, true)
 #undef QG_GV

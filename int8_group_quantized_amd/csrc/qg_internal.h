@@ -102,13 +102,15 @@ void small_plan_group(const SmallPlan& p, GroupArgs* g);
 hipError_t launch_gemm_small(int bits, const SmallPlan& p, const void* x, bool x_f16,
                              const GroupArgs& g, bool s_bf16, bool s_cbm, int64_t M, int64_t K,
                              void* workspace, hipStream_t st);
-// Decode GEMV (gemv.hip): the library's own plan for M = 1. One workgroup
-// per 16-column block (of every item of the group), gemv_k_waves(K)
-// wavefronts splitting K; no workspace.
+// Decode GEMV (gemv.hip): the library's own plan for M = 1, and for 2-16
+// rows where gemv_rows_fits (K of at most 40 groups, at most 512 column
+// blocks over all items). One workgroup per 16-column block (of every item
+// of the group), gemv_k_waves(K) wavefronts splitting K; no workspace.
 int gemv_k_waves(int64_t K);
+bool gemv_rows_fits(int64_t M, int64_t K, int64_t n_total);
 void gemv_group(GroupArgs* g);
 hipError_t launch_gemv(int bits, const void* x, bool x_f16, const GroupArgs& g, bool s_bf16,
-                       bool s_cbm, int64_t K, hipStream_t st);
+                       bool s_cbm, int64_t M, int64_t K, hipStream_t st);
 // Logical scales [K/128, N] -> column-block-major [N/16][K/128][16] (16-bit).
 hipError_t launch_prepack_scales(const void* scales, int64_t K, int64_t N, void* out,
                                  hipStream_t st);

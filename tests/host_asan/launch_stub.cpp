@@ -67,7 +67,8 @@ hipError_t launch_swa_attention(const SwaPlan&, const void*, const void*, const 
   return launched();
 }
 hipError_t launch_read_stream(const void*, int64_t, int, void*, hipStream_t) { return launched(); }
-hipError_t launch_gemv(int, const void*, bool, const GroupArgs&, bool, bool, int64_t, hipStream_t) {
+hipError_t launch_gemv(int, const void*, bool, const GroupArgs&, bool, bool, int64_t, int64_t,
+                       hipStream_t) {
   return launched();
 }
 hipError_t scratch_for_stream(hipStream_t, void** ptr) {
