@@ -63,9 +63,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only-headline", action="store_true", help="skip the other workloads")
     ap.add_argument("--workload", default="",
-                    help="run only the other workloads whose key contains this text (tiny, "
-                         "verify, drafter, prefill, fp16act, pack, dequant, fake_quant, "
-                         "grouped, attention)")
+                    help="run only the other workloads whose key contains one of these "
+                         "comma-separated texts (tiny, verify, drafter, prefill, fp16act, "
+                         "pack, dequant, fake_quant, grouped, attention)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 256 MiB device copy (reference for HBM byte counters)")
@@ -719,7 +719,7 @@ def main():
     extra = []
     if not args.only_headline:
         for key, fn in others:
-            if args.workload in key:
+            if any(w in key for w in args.workload.split(",")):
                 extra.append(fn())
                 log("row %s done" % key)
 
