@@ -2,6 +2,7 @@
 // workspace each plan needs. Plain C++ (no device code), shared by the
 // library and by a host-only build of the argument checks.
 #include <algorithm>
+#include <cmath>
 
 #include "qg_internal.h"
 
@@ -192,14 +193,27 @@ bool make_swa_plan(int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t S_max,
   // a sequence within the window (full attention, at most W keys) or the
   // block plus W / 2 keys before its first query.
   const int64_t span = w == 0 ? S_max : std::min<int64_t>(S_max, std::max<int64_t>(w, T + w / 2));
-  // About 384 workgroups over the whole call (a sweep of chunk sizes over the
-  // drafter's Long-context shapes at batch 1 and 8), and at least 256 keys
-  // (two 32-key steps per wavefront) per chunk: a cross-workgroup merge costs
-  // more than a short chunk saves.
+  // Key span of a sequence longer than the window: the block plus W / 2 keys
+  // before its first query; the chunk count is sized for it (a shorter
+  // sequence's full-attention span then takes more steps per wavefront).
+  const int64_t typ = w == 0 ? S_max : std::min<int64_t>(S_max, T + w / 2);
+  // Chunk count: each extra chunk adds its partial to the cross-workgroup
+  // merge, fewer chunks leave each workgroup more keys to stream. Sweeps of
+  // the drafter's Long-context shapes on MI355X: at batch 1 the best counts
+  // grow about as the cube root of the span (5 chunks for 528 keys, 6-7 for
+  // 1,040, ~9-12 for 8,208); with 128 or more query heads in the call a
+  // windowed span is fastest unsplit, and longer spans want at most about
+  // two workgroups per CU. A chunk shorter than about one 32-key step per
+  // wavefront saves less than its merge costs.
   const int64_t heads = std::max<int64_t>(1, B * Hq);
-  const int64_t target = std::max<int64_t>(1, std::min<int64_t>(64, (384 + heads - 1) / heads));
-  int64_t chunk = (span + target - 1) / target;
-  chunk = std::max<int64_t>(256, (chunk + 31) / 32 * 32);
+  int64_t n = 1;
+  if (!(heads >= 128 && typ <= 2048)) {
+    n = (int64_t)std::llround(0.6 * std::cbrt((double)typ));
+    n = std::min<int64_t>(n, std::max<int64_t>(1, 512 / heads));
+    n = std::max<int64_t>(1, std::min<int64_t>(n, typ / 96));   // >= 96 keys per chunk
+  }
+  int64_t chunk = (span + n - 1) / n;
+  chunk = (chunk + 31) / 32 * 32;
   if (chunk_req > 0) chunk = chunk_req;
   p->window = (int)w;
   p->chunk = (int)chunk;
