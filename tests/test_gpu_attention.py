@@ -84,6 +84,17 @@ def test_drafter_long_context_full_size(window):
     _parity(1, A["T"], A["Hq"], A["Hkv"], S, [S], window, 6000 + window)
 
 
+@pytest.mark.parametrize("window", [1024, 2048, 0])
+def test_batch8_long_context_plans(window):
+    # eight sequences of the drafter's heads over the Long cache, ragged: the
+    # library's plan runs windowed spans unsplit at 160 query heads and
+    # splits the full cache in three (every chunk count the batch-8 rows use)
+    A = workloads.ATTENTION
+    S = A["context"] + A["T"]
+    lens = [S, 5000, 1000, 600, S, 3000, 100, 2048]
+    _parity(8, A["T"], A["Hq"], A["Hkv"], S, lens, window, 6050 + window)
+
+
 @pytest.mark.parametrize("window", [0, 64, 256, 1024, 5, 1])
 def test_ragged_batch(window):
     # a long sequence, a medium one, one that is only the block, and one
