@@ -358,3 +358,20 @@ def test_decode_gemv_k_waves_and_rounds(bits, K, N):
     got = _run(bits, x, c, s, N)
     assert np.all(got[:, :16] == 0)
     _assert_close(got, gemm.gemm_ref(x, c, s, SDT[bits]), "K=%d N=%d" % (K, N))
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("M", [2, 5, 9, 16])
+@pytest.mark.parametrize("K,N", [(128, 16), (640, 48), (768, 32), (2560, 8192), (5120, 64),
+                                 (5248, 64), (2560, 8208)])
+def test_rows_gemv_rows_groups_and_limits(bits, M, K, N):
+    """2-16 rows on the library's own plan: 1, 5, 6, 20, 40 groups take the
+    rows GEMV (one to eight K-wavefronts, ragged last wavefronts), 41 groups
+    or 513 column blocks the staged kernel; rows past M are never written
+    (NaN-poisoned output), the first column block has all-zero codes and
+    must come out exactly 0."""
+    x, c, s = _inputs(bits, M, K, N, 1900 + 31 * M + K + N)
+    c[:, :16] = 0
+    got = _run(bits, x, c, s, N)
+    assert np.all(got[:, :16] == 0)
+    _assert_close(got, gemm.gemm_ref(x, c, s, SDT[bits]), "M=%d K=%d N=%d" % (M, K, N))
