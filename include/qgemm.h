@@ -90,7 +90,9 @@ size_t qg_packed_bytes(int bits, int64_t K, int64_t N);
 size_t qg_scale_bytes(int64_t K, int64_t N);
 
 /* Workspace the GEMM needs for this shape; 0 when the chosen plan needs
- * none (always 0 at M = 1, the decode GEMV). The first 65536 bytes of a workspace hold arrival counters: they must
+ * none (always 0 at M = 1, the decode GEMV, and at M = 2..16 for shapes of
+ * at most 40 groups and 512 column blocks, the 2-16-row GEMV). The first
+ * 65536 bytes of a workspace hold arrival counters: they must
  * be zero before the first call that uses the workspace, and every completed
  * call leaves them zero again. The rest holds fp32 split-K partial sums
  * (M <= 16) or, for INT4 with M > 16, the per-row, per-group activation sums
