@@ -62,6 +62,13 @@ def test_sizes():
     assert ws == 65536 + 4 * 3 * 64 * 4
     assert L.qg_workspace_bytes_plan(4, 3, 1024, 64, 1, 1, 1) == 0
     assert L.qg_workspace_bytes_plan(4, 3, 1024, 64, 3, 1, 1) == 0   # bad plan -> 0
+    # the library's own plans: the decode GEMV and the 2-16-row GEMV (at most
+    # 40 groups and 512 column blocks) need none; the M = 16 down shape
+    # splits K and does
+    assert L.qg_workspace_bytes(4, 1, 9728, 2560) == 0
+    assert L.qg_workspace_bytes(8, 16, 2560, 3584) == 0
+    assert L.qg_workspace_bytes(4, 16, 5120, 8192) == 0
+    assert L.qg_workspace_bytes(4, 16, 9728, 2560) > 65536
 
 
 def _gemm(M=1, K=256, N=512, x=FAKE, w=FAKE, s=FAKE, sdt=1, out=FAKE, ws=0, wsb=0, bits=4):
