@@ -222,6 +222,9 @@ bool make_swa_plan(int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t S_max,
   p->units = (int)units;
   if (p->nchunks > kSwaMaxChunks) return false;
   p->grid = (int)(8 * (Hq / Hkv) * ((units + 7) / 8));
+  // At most two 32-key steps per wavefront in a typical chunk: the queries
+  // go through LDS once per workgroup.
+  p->q_lds = (typ + p->nchunks - 1) / p->nchunks <= 2 * 4 * 32;
   return units < (1 << 24);
 }
 

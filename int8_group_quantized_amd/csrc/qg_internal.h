@@ -124,6 +124,7 @@ struct SwaPlan {
   int nchunks = 1;
   int units = 0;
   int grid = 0;
+  bool q_lds = false;   // queries staged once per workgroup in LDS (short chunks)
 };
 bool make_swa_plan(int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t S_max, int64_t window,
                    int64_t chunk, SwaPlan* p);
