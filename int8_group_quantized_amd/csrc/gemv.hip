@@ -24,7 +24,11 @@
 //   * the scale of the lane's column is a 2-byte load per group (either
 //     scale order), issued with the group's other loads;
 //   * wavefronts that split K are summed through LDS in wave order after
-//     one barrier (deterministic); lanes 0..15 store the 16 outputs.
+//     one barrier (deterministic); lanes 0..15 store the 16 outputs;
+//   * the scale order is a template parameter and the round loop exits on a
+//     scalar test of the next round's first group: with the order chosen by
+//     a runtime branch inside the loop, the same arithmetic measured 6.12
+//     against 5.90 us (gate/up) and 4.98 against 4.89 us (down).
 // Workgroups are dealt to the eight XCDs round-robin; each XCD gets a
 // contiguous run of column blocks, so the four blocks sharing a 128-byte scale
 // line are read by one XCD's L2.
@@ -46,9 +50,9 @@ __device__ __forceinline__ uint32_t gemv_opaque(uint32_t m) {
   return m;
 }
 
-template <int BITS, bool SBF, bool XH, bool GR, int WK>
-__global__ __launch_bounds__(64 * WK) void gemv_kernel(const uint16_t* __restrict__ x, int K,
-                                                       int rounds, int scbm, const GroupArgs ga) {
+template <int BITS, bool SBF, bool XH, bool GR, int WK, bool SCBM>
+__global__ __launch_bounds__(64 * WK) void gemv_kernel(const uint16_t* __restrict__ x, int G,
+                                                       const GroupArgs ga) {
   using A = Act<XH>;
   constexpr int TB = (BITS == 4) ? 1024 : 2048;   // bytes per 16 x 128 tile
   constexpr int TW = TB / 1024;                   // 16-byte loads per lane per tile
@@ -70,23 +74,25 @@ __global__ __launch_bounds__(64 * WK) void gemv_kernel(const uint16_t* __restric
   const GroupItem& it = ga.item[item];
   const int N = it.n;
   const int cb = b - (GR ? it.wg_first : 0);
-  const int G = K >> 7;
+  const char* __restrict__ packed = it.packed;
+  const uint16_t* __restrict__ scales = it.scales;
+  uint16_t* __restrict__ out = it.out;
   const uint32_t magic = gemv_opaque(A::kMagic);
   const u32x4 off = {A::kOffset, A::kOffset, A::kOffset, A::kOffset};
   // A operand: lane (row l16, K slice lq) takes elements 32 (l16 % 4) + 8 lq .. + 8
   const int xoff = (32 * (l16 & 3) + 8 * lq) * 2;
 
   float acc = 0.0f;
-  for (int r = 0; r < rounds; ++r) {
-    const int g0 = min((r * WK + wave) * kGW, G);
+  for (int r = 0;; ++r) {
+    const int g0 = (r * WK + wave) * kGW;
+    if (g0 >= G) break;                           // wave-uniform: later rounds are empty too
     const int wn = min(kGW, G - g0);              // groups of this wavefront this round
-    if (wn <= 0) break;                           // wave-uniform: later rounds are empty too
     const __amdgpu_buffer_rsrc_t xr = gemv_rsrc(x + (int64_t)g0 * kGroup, wn * kGroup * 2);
-    const __amdgpu_buffer_rsrc_t tr = gemv_rsrc(it.packed + ((int64_t)cb * G + g0) * TB, wn * TB);
+    const __amdgpu_buffer_rsrc_t tr = gemv_rsrc(packed + ((int64_t)cb * G + g0) * TB, wn * TB);
     const __amdgpu_buffer_rsrc_t sr =
-        scbm ? gemv_rsrc(it.scales + ((int64_t)cb * G + g0) * 16, wn * 32)
-             : gemv_rsrc(it.scales + (int64_t)g0 * N + cb * 16, ((wn - 1) * N + 16) * 2);
-    const int sstride = scbm ? 16 : N;
+        SCBM ? gemv_rsrc(scales + ((int64_t)cb * G + g0) * 16, wn * 32)
+             : gemv_rsrc(scales + (int64_t)g0 * N + cb * 16, ((wn - 1) * N + 16) * 2);
+    const int sstride = SCBM ? 16 : N;
 
     u32x4 xa[kGW];
     u32x4 t[kGW][TW];
@@ -137,7 +143,7 @@ __global__ __launch_bounds__(64 * WK) void gemv_kernel(const uint16_t* __restric
 #pragma unroll
     for (int w = 0; w < WK - 1; ++w) acc += red[w * 16 + l16];
   }
-  if (lq == 0) it.out[cb * 16 + l16] = A::out(acc);
+  if (lq == 0) out[cb * 16 + l16] = A::out(acc);
 }
 
 // The same structure for 2-16 rows (a verification block), where the shape
@@ -148,10 +154,9 @@ __global__ __launch_bounds__(64 * WK) void gemv_kernel(const uint16_t* __restric
 // for all-zero code columns). x is re-read from L2 by every column block;
 // that costs less than staging it behind a barrier while the column blocks
 // are few (wide shapes use the staged small-M kernel).
-template <int BITS, bool SBF, bool XH, bool GR, int WK>
+template <int BITS, bool SBF, bool XH, bool GR, int WK, bool SCBM>
 __global__ __launch_bounds__(64 * WK) void gemv_rows_kernel(const uint16_t* __restrict__ x, int M,
-                                                            int K, int rounds, int scbm,
-                                                            const GroupArgs ga) {
+                                                            int K, const GroupArgs ga) {
   using A = Act<XH>;
   constexpr int TB = (BITS == 4) ? 1024 : 2048;
   constexpr int TW = TB / 1024;
@@ -173,6 +178,9 @@ __global__ __launch_bounds__(64 * WK) void gemv_rows_kernel(const uint16_t* __re
   const GroupItem& it = ga.item[item];
   const int N = it.n;
   const int cb = b - (GR ? it.wg_first : 0);
+  const char* __restrict__ packed = it.packed;
+  const uint16_t* __restrict__ scales = it.scales;
+  uint16_t* __restrict__ out = it.out;
   const int G = K >> 7;
   const uint32_t magic = gemv_opaque(A::kMagic);
   const u32x4 off = {A::kOffset, A::kOffset, A::kOffset, A::kOffset};
@@ -182,15 +190,15 @@ __global__ __launch_bounds__(64 * WK) void gemv_rows_kernel(const uint16_t* __re
   const int xrow = l16 * K * 2 + 16 * lq;
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int r = 0; r < rounds; ++r) {
-    const int g0 = min((r * WK + wave) * kGW, G);
+  for (int r = 0;; ++r) {
+    const int g0 = (r * WK + wave) * kGW;
+    if (g0 >= G) break;                           // wave-uniform: later rounds are empty too
     const int wn = min(kGW, G - g0);
-    if (wn <= 0) break;
-    const __amdgpu_buffer_rsrc_t tr = gemv_rsrc(it.packed + ((int64_t)cb * G + g0) * TB, wn * TB);
+    const __amdgpu_buffer_rsrc_t tr = gemv_rsrc(packed + ((int64_t)cb * G + g0) * TB, wn * TB);
     const __amdgpu_buffer_rsrc_t sr =
-        scbm ? gemv_rsrc(it.scales + ((int64_t)cb * G + g0) * 16, wn * 32)
-             : gemv_rsrc(it.scales + (int64_t)g0 * N + cb * 16, ((wn - 1) * N + 16) * 2);
-    const int sstride = scbm ? 16 : N;
+        SCBM ? gemv_rsrc(scales + ((int64_t)cb * G + g0) * 16, wn * 32)
+             : gemv_rsrc(scales + (int64_t)g0 * N + cb * 16, ((wn - 1) * N + 16) * 2);
+    const int sstride = SCBM ? 16 : N;
 
     u32x4 xa[kGW][4];
     u32x4 t[kGW][TW];
@@ -248,34 +256,31 @@ __global__ __launch_bounds__(64 * WK) void gemv_rows_kernel(const uint16_t* __re
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int row = 4 * lq + e;
-    if (row < M) it.out[(int64_t)row * N + cb * 16 + l16] = A::out(acc[e]);
+    if (row < M) out[(int64_t)row * N + cb * 16 + l16] = A::out(acc[e]);
   }
 }
 
-template <int BITS, bool SBF, bool XH, bool GR>
-hipError_t launch_wk(int wk, const void* x, const GroupArgs& g, bool s_cbm, int64_t M, int64_t K,
+template <int BITS, bool SBF, bool XH, bool GR, bool SCBM>
+hipError_t launch_wk(int wk, const void* x, const GroupArgs& g, int64_t M, int64_t K,
                      hipStream_t st) {
-  const int G = (int)(K / kGroup);
-  const int rounds = (G + wk * kGW - 1) / (wk * kGW);
   const auto* xp = static_cast<const uint16_t*>(x);
-  const int scbm = s_cbm ? 1 : 0;
-  const int m = (int)M, k = (int)K;
+  const int m = (int)M, k = (int)K, G = (int)(K / kGroup);
   const dim3 grid((unsigned)g.wg_total);
   if (M == 1) {
     switch (wk) {
-      case 1: gemv_kernel<BITS, SBF, XH, GR, 1><<<grid, 64, 0, st>>>(xp, k, rounds, scbm, g); break;
-      case 2: gemv_kernel<BITS, SBF, XH, GR, 2><<<grid, 128, 0, st>>>(xp, k, rounds, scbm, g); break;
-      case 4: gemv_kernel<BITS, SBF, XH, GR, 4><<<grid, 256, 0, st>>>(xp, k, rounds, scbm, g); break;
-      case 8: gemv_kernel<BITS, SBF, XH, GR, 8><<<grid, 512, 0, st>>>(xp, k, rounds, scbm, g); break;
-      case 16: gemv_kernel<BITS, SBF, XH, GR, 16><<<grid, 1024, 0, st>>>(xp, k, rounds, scbm, g); break;
+      case 1: gemv_kernel<BITS, SBF, XH, GR, 1, SCBM><<<grid, 64, 0, st>>>(xp, G, g); break;
+      case 2: gemv_kernel<BITS, SBF, XH, GR, 2, SCBM><<<grid, 128, 0, st>>>(xp, G, g); break;
+      case 4: gemv_kernel<BITS, SBF, XH, GR, 4, SCBM><<<grid, 256, 0, st>>>(xp, G, g); break;
+      case 8: gemv_kernel<BITS, SBF, XH, GR, 8, SCBM><<<grid, 512, 0, st>>>(xp, G, g); break;
+      case 16: gemv_kernel<BITS, SBF, XH, GR, 16, SCBM><<<grid, 1024, 0, st>>>(xp, G, g); break;
       default: return hipErrorInvalidValue;
     }
   } else {
     switch (wk) {
-      case 1: gemv_rows_kernel<BITS, SBF, XH, GR, 1><<<grid, 64, 0, st>>>(xp, m, k, rounds, scbm, g); break;
-      case 2: gemv_rows_kernel<BITS, SBF, XH, GR, 2><<<grid, 128, 0, st>>>(xp, m, k, rounds, scbm, g); break;
-      case 4: gemv_rows_kernel<BITS, SBF, XH, GR, 4><<<grid, 256, 0, st>>>(xp, m, k, rounds, scbm, g); break;
-      case 8: gemv_rows_kernel<BITS, SBF, XH, GR, 8><<<grid, 512, 0, st>>>(xp, m, k, rounds, scbm, g); break;
+      case 1: gemv_rows_kernel<BITS, SBF, XH, GR, 1, SCBM><<<grid, 64, 0, st>>>(xp, m, k, g); break;
+      case 2: gemv_rows_kernel<BITS, SBF, XH, GR, 2, SCBM><<<grid, 128, 0, st>>>(xp, m, k, g); break;
+      case 4: gemv_rows_kernel<BITS, SBF, XH, GR, 4, SCBM><<<grid, 256, 0, st>>>(xp, m, k, g); break;
+      case 8: gemv_rows_kernel<BITS, SBF, XH, GR, 8, SCBM><<<grid, 512, 0, st>>>(xp, m, k, g); break;
       default: return hipErrorInvalidValue;
     }
   }
@@ -285,8 +290,11 @@ hipError_t launch_wk(int wk, const void* x, const GroupArgs& g, bool s_cbm, int6
 template <int BITS, bool SBF, bool XH>
 hipError_t launch_gr(int wk, const void* x, const GroupArgs& g, bool s_cbm, int64_t M, int64_t K,
                      hipStream_t st) {
-  return g.count > 1 ? launch_wk<BITS, SBF, XH, true>(wk, x, g, s_cbm, M, K, st)
-                     : launch_wk<BITS, SBF, XH, false>(wk, x, g, s_cbm, M, K, st);
+  if (g.count > 1)
+    return s_cbm ? launch_wk<BITS, SBF, XH, true, true>(wk, x, g, M, K, st)
+                 : launch_wk<BITS, SBF, XH, true, false>(wk, x, g, M, K, st);
+  return s_cbm ? launch_wk<BITS, SBF, XH, false, true>(wk, x, g, M, K, st)
+               : launch_wk<BITS, SBF, XH, false, false>(wk, x, g, M, K, st);
 }
 
 }  // namespace
