@@ -197,26 +197,32 @@ __global__ __launch_bounds__(256, 2) void swa_attention_kernel(
   for (; s < nsteps; s += kWaves) {
     const int key0 = k0 + 32 * s;
     const bool more = s + kWaves < nsteps;
+    // Scores for two 16-key blocks; the next step's rows are requested once
+    // these products have their operands (a fetch issued before them made
+    // the products wait on it).
+    f32x4 acc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      acc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kc[kb][j]),
+                                                          __builtin_bit_cast(bf16x8, qop(j)),
+                                                          acc[kb], 0, 0, 0);
+    }
     u32x4 kn[2][4];
     if (more) {
       load_k(kn, key0 + 32 * kWaves);
       load_v(key0 + 32 * kWaves);
     }
-    // Scores for two 16-key blocks.
     float sc[2][4];
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kc[kb][j]),
-                                                      __builtin_bit_cast(bf16x8, qop(j)), acc, 0,
-                                                      0, 0);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int key = key0 + 16 * kb + 4 * g + e;
-        sc[kb][e] = (key >= vlo && key < vhi) ? acc[e] * scale_log2 : -INFINITY;
+        sc[kb][e] = (key >= vlo && key < vhi) ? acc[kb][e] * scale_log2 : -INFINITY;
         mx = fmaxf(mx, sc[kb][e]);
       }
     }
