@@ -318,16 +318,25 @@ qg_status qg_swa_attention(const void* q, const void* k_cache, const void* v_cac
                            int64_t Hq, int64_t Hkv, int64_t D, int64_t S_max,
                            int64_t window, float scale, void* workspace,
                            size_t workspace_bytes, void* stream);
-/* The same with the number of keys per workgroup chosen by the caller (a
- * multiple of 32; 0 picks the library's own), for tests and tuning. */
-size_t qg_swa_workspace_bytes_chunk(int64_t B, int64_t T, int64_t Hq, int64_t Hkv,
-                                    int64_t D, int64_t S_max, int64_t window,
-                                    int64_t chunk);
-qg_status qg_swa_attention_chunk(const void* q, const void* k_cache, const void* v_cache,
-                                 const int32_t* seq_lens, void* out, int64_t B, int64_t T,
-                                 int64_t Hq, int64_t Hkv, int64_t D, int64_t S_max,
-                                 int64_t window, float scale, int64_t chunk, void* workspace,
-                                 size_t workspace_bytes, void* stream);
+/* The same with the work split chosen by the caller, for tests and tuning.
+ *   chunk  keys per workgroup: a multiple of 32, or 0 for the library's own
+ *   heads  query heads per workgroup: 0 lets the library choose; 1 runs one
+ *          query head per workgroup; 2, 3, 4, 5, 6 or 8 (a divisor of
+ *          Hq / Hkv) runs that many heads of one KV head per workgroup over
+ *          one shared stream of its K/V rows, with at most 16 chunks
+ * Results match qg_swa_attention's to the summation order of the chunks.
+ * Errors as qg_swa_attention, plus QG_ERR_SHAPE for a heads value outside
+ * that list or a split with too many chunks; the workspace size depends on
+ * both values, and qg_swa_workspace_bytes_plan returns 0 for a split that
+ * cannot run. */
+size_t qg_swa_workspace_bytes_plan(int64_t B, int64_t T, int64_t Hq, int64_t Hkv,
+                                   int64_t D, int64_t S_max, int64_t window,
+                                   int64_t chunk, int64_t heads);
+qg_status qg_swa_attention_plan(const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* seq_lens, void* out, int64_t B, int64_t T,
+                                int64_t Hq, int64_t Hkv, int64_t D, int64_t S_max,
+                                int64_t window, float scale, int64_t chunk, int64_t heads,
+                                void* workspace, size_t workspace_bytes, void* stream);
 
 /* qgemm_w4a16 for callers that cannot allocate device memory: code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.

@@ -73,10 +73,10 @@ _SIGNATURES = {
     "qgemm_w8f16_grouped": ([_P, _ITEMS, _INT, _INT, _I64, _I64, _P, _SZ, _P], _INT),
     "qg_dequant_w8": ([_P, _P, _INT, _I64, _I64, _P, _INT, _P], _INT),
     "qg_swa_workspace_bytes": ([_I64] * 7, _SZ),
-    "qg_swa_workspace_bytes_chunk": ([_I64] * 8, _SZ),
+    "qg_swa_workspace_bytes_plan": ([_I64] * 9, _SZ),
     "qg_swa_attention": ([_P, _P, _P, _P, _P] + [_I64] * 7 + [ctypes.c_float, _P, _SZ, _P], _INT),
-    "qg_swa_attention_chunk": ([_P, _P, _P, _P, _P] + [_I64] * 7 + [ctypes.c_float, _I64, _P, _SZ,
-                                                                     _P], _INT),
+    "qg_swa_attention_plan": ([_P, _P, _P, _P, _P] + [_I64] * 7 + [ctypes.c_float, _I64, _I64, _P,
+                                                                    _SZ, _P], _INT),
     "qg_read_stream": ([_P, _SZ, _INT, _P, _P], _INT),
     "qg_prepack_scales": ([_P, _INT, _I64, _I64, _P, _P], _INT),
     "qg_noalloc_scratch_bytes": ([], _SZ),
@@ -439,12 +439,16 @@ def qgemm_grouped(x, weights, bits, outs=None, ws=None, scales_cbm=False):
     return outs
 
 
-def swa_attention(q, k_cache, v_cache, seq_lens, window, scale=None, out=None, ws=None, chunk=0):
+def swa_attention(q, k_cache, v_cache, seq_lens, window, scale=None, out=None, ws=None, chunk=0,
+                  heads=0):
     """Drafter attention with a symmetric sliding window over a full KV cache.
 
     q [B, T, Hq, 128] bf16; k_cache, v_cache [B, S_max, Hkv, 128] bf16;
     seq_lens int32 [B] on the device (cache entries per sequence, the block's
     T included); window 0 for full attention. Returns out [B, T, Hq, 128].
+    chunk (keys per workgroup) and heads (query heads per workgroup: 1, or
+    2-6 / 8 for the shared K/V stream) override the library's split; 0 keeps
+    its choice.
     """
     _need_cuda(q, k_cache, v_cache, seq_lens)
     if q.dtype != torch.bfloat16 or k_cache.dtype != torch.bfloat16 or v_cache.dtype != torch.bfloat16:
@@ -464,13 +468,13 @@ def swa_attention(q, k_cache, v_cache, seq_lens, window, scale=None, out=None, w
         scale = 1.0 / math.sqrt(D)
     if out is None:
         out = torch.empty_like(q)
-    need = int(lib().qg_swa_workspace_bytes_chunk(B, T, Hq, Hkv, D, S_max, window, chunk))
+    need = int(lib().qg_swa_workspace_bytes_plan(B, T, Hq, Hkv, D, S_max, window, chunk, heads))
     if ws is None and need > 0:
         ws = workspace(q.device, need)
     ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
-    _check("qg_swa_attention", lib().qg_swa_attention_chunk(
+    _check("qg_swa_attention", lib().qg_swa_attention_plan(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), _ptr(out), B, T, Hq, Hkv, D, S_max,
-        window, scale, chunk, _ptr(ws), ws_bytes, _stream(q)))
+        window, scale, chunk, heads, _ptr(ws), ws_bytes, _stream(q)))
     return out
 
 

@@ -281,32 +281,34 @@ size_t workspace_bytes(int bits, int64_t M, int64_t K, int64_t N, int nbw, int w
 constexpr int64_t kSwaMaxPairs = 65536 / 4;   // arrival counters at the workspace start
 
 qg_status swa_check(int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t D, int64_t S_max,
-                    int64_t window, int64_t chunk, qg::SwaPlan* plan) {
+                    int64_t window, int64_t chunk, int64_t heads, qg::SwaPlan* plan) {
   if (B < 0 || B > kMaxM || T < 1 || T > 16 || D != 128 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0)
     return QG_ERR_SHAPE;
   if (S_max < T || window < 0 || chunk < 0 || chunk % 32 != 0 || chunk > (int64_t(1) << 20))
     return QG_ERR_SHAPE;
+  if (heads < 0 || heads > 8) return QG_ERR_SHAPE;
   if (Hq > 4096 || S_max * Hkv * D * 2 >= kMaxElems || T * Hq * D * 2 >= kMaxElems)
     return QG_ERR_SHAPE;
-  if (!qg::make_swa_plan(B, T, Hq, Hkv, S_max, window, chunk, plan)) return QG_ERR_SHAPE;
+  if (!qg::make_swa_plan(B, T, Hq, Hkv, S_max, window, chunk, heads, plan)) return QG_ERR_SHAPE;
   if (plan->nchunks > 1 && B * Hq > kSwaMaxPairs) return QG_ERR_SHAPE;
   if ((int64_t)plan->grid >= kMaxElems) return QG_ERR_SHAPE;
   return QG_OK;
 }
 
 size_t swa_workspace_bytes(int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t D,
-                           int64_t S_max, int64_t window, int64_t chunk) {
+                           int64_t S_max, int64_t window, int64_t chunk, int64_t heads) {
   qg::SwaPlan plan;
-  if (swa_check(B, T, Hq, Hkv, D, S_max, window, chunk, &plan) != QG_OK || B == 0) return 0;
+  if (swa_check(B, T, Hq, Hkv, D, S_max, window, chunk, heads, &plan) != QG_OK || B == 0)
+    return 0;
   return qg::swa_workspace(plan, B, Hq);
 }
 
 qg_status swa_attention(const void* q, const void* k, const void* v, const int32_t* seq_lens,
                         void* out, int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t D,
-                        int64_t S_max, int64_t window, float scale, int64_t chunk, void* ws,
-                        size_t ws_bytes, void* stream) {
+                        int64_t S_max, int64_t window, float scale, int64_t chunk,
+                        int64_t heads, void* ws, size_t ws_bytes, void* stream) {
   qg::SwaPlan plan;
-  qg_status s = swa_check(B, T, Hq, Hkv, D, S_max, window, chunk, &plan);
+  qg_status s = swa_check(B, T, Hq, Hkv, D, S_max, window, chunk, heads, &plan);
   if (s != QG_OK) return s;
   if (!(scale == scale) || scale == INFINITY || scale == -INFINITY) return QG_ERR_SHAPE;
   if (B == 0) return QG_OK;
@@ -525,7 +527,7 @@ qg_status qgemm_w8f16_grouped(const void* x, const qg_group_item* items, int cou
 
 size_t qg_swa_workspace_bytes(int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t D,
                               int64_t S_max, int64_t window) {
-  return swa_workspace_bytes(B, T, Hq, Hkv, D, S_max, window, 0);
+  return swa_workspace_bytes(B, T, Hq, Hkv, D, S_max, window, 0, 0);
 }
 
 qg_status qg_swa_attention(const void* q, const void* k_cache, const void* v_cache,
@@ -533,21 +535,22 @@ qg_status qg_swa_attention(const void* q, const void* k_cache, const void* v_cac
                            int64_t Hkv, int64_t D, int64_t S_max, int64_t window, float scale,
                            void* workspace, size_t workspace_bytes, void* stream) {
   return swa_attention(q, k_cache, v_cache, seq_lens, out, B, T, Hq, Hkv, D, S_max, window,
-                       scale, 0, workspace, workspace_bytes, stream);
+                       scale, 0, 0, workspace, workspace_bytes, stream);
 }
 
-size_t qg_swa_workspace_bytes_chunk(int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t D,
-                                    int64_t S_max, int64_t window, int64_t chunk) {
-  return swa_workspace_bytes(B, T, Hq, Hkv, D, S_max, window, chunk);
+size_t qg_swa_workspace_bytes_plan(int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t D,
+                                   int64_t S_max, int64_t window, int64_t chunk,
+                                   int64_t heads) {
+  return swa_workspace_bytes(B, T, Hq, Hkv, D, S_max, window, chunk, heads);
 }
 
-qg_status qg_swa_attention_chunk(const void* q, const void* k_cache, const void* v_cache,
-                                 const int32_t* seq_lens, void* out, int64_t B, int64_t T,
-                                 int64_t Hq, int64_t Hkv, int64_t D, int64_t S_max,
-                                 int64_t window, float scale, int64_t chunk, void* workspace,
-                                 size_t workspace_bytes, void* stream) {
+qg_status qg_swa_attention_plan(const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* seq_lens, void* out, int64_t B, int64_t T,
+                                int64_t Hq, int64_t Hkv, int64_t D, int64_t S_max,
+                                int64_t window, float scale, int64_t chunk, int64_t heads,
+                                void* workspace, size_t workspace_bytes, void* stream) {
   return swa_attention(q, k_cache, v_cache, seq_lens, out, B, T, Hq, Hkv, D, S_max, window,
-                       scale, chunk, workspace, workspace_bytes, stream);
+                       scale, chunk, heads, workspace, workspace_bytes, stream);
 }
 
 qg_status qg_prepack_scales(const void* scales, qg_dtype s_dt, int64_t K, int64_t N, void* out,

@@ -187,7 +187,7 @@ size_t prefill_workspace(int bits, const PrefillPlan& p, int64_t K) {
 // ---- drafter attention ----
 
 bool make_swa_plan(int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t S_max, int64_t window,
-                   int64_t chunk_req, SwaPlan* p) {
+                   int64_t chunk_req, int64_t heads_req, SwaPlan* p) {
   const int64_t w = window >= S_max ? 0 : window;   // a window past every sequence is no window
   // Longest key span of any sequence: the whole cache without a window; else
   // a sequence within the window (full attention, at most W keys) or the
@@ -197,20 +197,48 @@ bool make_swa_plan(int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t S_max,
   // before its first query; the chunk count is sized for it (a shorter
   // sequence's full-attention span then takes more steps per wavefront).
   const int64_t typ = w == 0 ? S_max : std::min<int64_t>(S_max, T + w / 2);
-  // Chunk count: each extra chunk adds its partial to the cross-workgroup
-  // merge, fewer chunks leave each workgroup more keys to stream. Sweeps of
-  // the drafter's Long-context shapes on MI355X: at batch 1 the best counts
-  // grow about as the cube root of the span (5 chunks for 528 keys, 6-7 for
-  // 1,040, ~9-12 for 8,208); with 128 or more query heads in the call a
-  // windowed span is fastest unsplit, and longer spans want at most about
-  // two workgroups per CU. A chunk shorter than about one 32-key step per
-  // wavefront saves less than its merge costs.
-  const int64_t heads = std::max<int64_t>(1, B * Hq);
+  const int64_t G = Hq / Hkv;
+  auto ring_ok = [&](int64_t h) {
+    return (h == 2 || h == 3 || h == 4 || h == 5 || h == 6 || h == 8) && G % h == 0;
+  };
+  int64_t ring = 0;
+  if (heads_req > 1) {
+    if (!ring_ok(heads_req)) return false;
+    ring = heads_req;
+  } else if (heads_req == 0 && chunk_req == 0) {
+    // The shared-ring kernel reads each K/V row once for up to eight query
+    // heads; it pays off on long spans once the (sequence, KV head, head
+    // group) count fills the GPU at about eight chunks each (MI355X, the
+    // drafter's Long-context shapes: batch 8, 20 query over 4 KV heads, full
+    // attention over 8,208 keys: 38 us against 67 us for one head per
+    // workgroup; windowed spans and batch 1 stay faster one head each).
+    int64_t h = 0;
+    for (int64_t c : {8, 6, 5, 4, 3, 2})
+      if (h == 0 && ring_ok(c)) h = c;
+    const int64_t groups = h > 0 ? B * Hkv * (G / h) : 0;
+    if (h > 0 && typ >= 4096 && groups >= 32 && groups <= 256) ring = h;
+  }
   int64_t n = 1;
-  if (!(heads >= 128 && typ <= 2048)) {
-    n = (int64_t)std::llround(0.6 * std::cbrt((double)typ));
-    n = std::min<int64_t>(n, std::max<int64_t>(1, 512 / heads));
-    n = std::max<int64_t>(1, std::min<int64_t>(n, typ / 96));   // >= 96 keys per chunk
+  if (ring > 0) {
+    // About 256 workgroups, at least 512 keys per chunk.
+    const int64_t groups = B * Hkv * (G / ring);
+    n = std::max<int64_t>(1, std::min<int64_t>(256 / std::max<int64_t>(1, groups), typ / 512));
+    n = std::min<int64_t>(n, kSwaRingMaxChunks);
+  } else {
+    // Chunk count: each extra chunk adds its partial to the cross-workgroup
+    // merge, fewer chunks leave each workgroup more keys to stream. Sweeps of
+    // the drafter's Long-context shapes on MI355X: at batch 1 the best counts
+    // grow about as the cube root of the span (5 chunks for 528 keys, 6-7 for
+    // 1,040, ~9-12 for 8,208); with 128 or more query heads in the call a
+    // windowed span is fastest unsplit, and longer spans want at most about
+    // two workgroups per CU. A chunk shorter than about one 32-key step per
+    // wavefront saves less than its merge costs.
+    const int64_t heads = std::max<int64_t>(1, B * Hq);
+    if (!(heads >= 128 && typ <= 2048)) {
+      n = (int64_t)std::llround(0.6 * std::cbrt((double)typ));
+      n = std::min<int64_t>(n, std::max<int64_t>(1, 512 / heads));
+      n = std::max<int64_t>(1, std::min<int64_t>(n, typ / 96));   // >= 96 keys per chunk
+    }
   }
   int64_t chunk = (span + n - 1) / n;
   chunk = (chunk + 31) / 32 * 32;
@@ -218,14 +246,25 @@ bool make_swa_plan(int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t S_max,
   p->window = (int)w;
   p->chunk = (int)chunk;
   p->nchunks = (int)((span + chunk - 1) / chunk);
+  p->ring = (int)ring;
+  if (p->nchunks > (ring > 0 ? kSwaRingMaxChunks : kSwaMaxChunks)) return false;
+  if (ring > 0) {
+    const int64_t units = B * Hkv * (G / ring) * p->nchunks;
+    if (units >= (1 << 24)) return false;
+    p->units = (int)units;
+    p->grid = (int)units;
+    p->q_lds = false;
+    return true;
+  }
   const int64_t units = B * Hkv * p->nchunks;
+  const int64_t grid = 8 * G * ((units + 7) / 8);
+  if (units >= (1 << 24) || grid > 0x7FFFFFFF) return false;
   p->units = (int)units;
-  if (p->nchunks > kSwaMaxChunks) return false;
-  p->grid = (int)(8 * (Hq / Hkv) * ((units + 7) / 8));
+  p->grid = (int)grid;
   // At most two 32-key steps per wavefront in a typical chunk: the queries
   // go through LDS once per workgroup.
   p->q_lds = (typ + p->nchunks - 1) / p->nchunks <= 2 * 4 * 32;
-  return units < (1 << 24);
+  return true;
 }
 
 size_t swa_workspace(const SwaPlan& p, int64_t B, int64_t Hq) {

@@ -16,6 +16,7 @@ constexpr uint32_t kCounterBytes = 65536;   // arrival counters at a workspace's
 constexpr int kPrefillRows = 64;            // rows of a prefill tile
 constexpr int kGemvGroups = 5;              // groups per decode-GEMV wavefront per round
 constexpr int kSwaMaxChunks = 256;          // key chunks one (sequence, head) may have
+constexpr int kSwaRingMaxChunks = 16;       // the same for the shared-ring kernel (merge table)
 constexpr int kSwaPartFloats = 16 * 128 + 32;   // a chunk's record: O[16][128], max[16], sum[16]
 
 // Small-M tiling: each wavefront covers `nbw` 16-column blocks; `wk`
@@ -125,9 +126,15 @@ struct SwaPlan {
   int units = 0;
   int grid = 0;
   bool q_lds = false;   // queries staged once per workgroup in LDS (short chunks)
+  int ring = 0;         // > 0: that many query heads of one KV head per workgroup
+                        // over a shared K/V ring (units then count sequence x KV
+                        // head x head group x chunk); 0: one query head each
 };
+// chunk: keys per workgroup, 0 for the library's choice; heads: query heads
+// per workgroup, 0 for the library's choice, 1 for the one-head kernel, 2-6
+// or 8 (dividing Hq / Hkv) for the shared-ring kernel. False when no plan fits.
 bool make_swa_plan(int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t S_max, int64_t window,
-                   int64_t chunk, SwaPlan* p);
+                   int64_t chunk, int64_t heads, SwaPlan* p);
 size_t swa_workspace(const SwaPlan& p, int64_t B, int64_t Hq);
 hipError_t launch_swa_attention(const SwaPlan& p, const void* q, const void* k, const void* v,
                                 const int32_t* seq_lens, void* out, int64_t T, int64_t Hq,

@@ -325,18 +325,21 @@ __global__ __launch_bounds__(256, 2) void swa_attention_kernel(
   // Split across workgroups: publish this chunk, count the arrival. The
   // region of one (sequence, head) holds every chunk's O[16][128], then every
   // chunk's max[16] and sum[16], so the merge reads the maxima in one sweep.
+  // A chunk's O is stored thread-major: 16-byte word 256 j + tid holds this
+  // thread's dims d0 + 4 j .. +3, so each store and each merge load of a
+  // wavefront moves 1 KB of consecutive bytes.
   const size_t pbase = ((size_t)(b * Hq + h) * nchunks) * kPartFloats;
   const uint32_t ml0 = (uint32_t)(nchunks * kOFloats * sizeof(float));
   const __amdgpu_buffer_rsrc_t rp =
       rsrc(partials + pbase, (uint32_t)(nchunks * kPartFloats * sizeof(float)));
   {
-    const uint32_t off = (uint32_t)((c * kOFloats + rt * kD + d0) * sizeof(float));
+    const uint32_t off = (uint32_t)((c * kOFloats + 4 * tid) * sizeof(float));
     __builtin_amdgcn_raw_buffer_store_b128(u32x4{__float_as_uint(acc[0]), __float_as_uint(acc[1]),
                                                  __float_as_uint(acc[2]), __float_as_uint(acc[3])},
                                            rp, off, 0, kCoherent);
     __builtin_amdgcn_raw_buffer_store_b128(u32x4{__float_as_uint(acc[4]), __float_as_uint(acc[5]),
                                                  __float_as_uint(acc[6]), __float_as_uint(acc[7])},
-                                           rp, off + 16, 0, kCoherent);
+                                           rp, off + 4096, 0, kCoherent);
     if ((tid & 15) == 0) {
       const uint32_t moff = ml0 + (uint32_t)((c * 32 + rt) * sizeof(float));
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(M), rp, moff, 0, kCoherent);
@@ -366,10 +369,10 @@ __global__ __launch_bounds__(256, 2) void swa_attention_kernel(
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
       const uint32_t off = c0 + i < nchunks
-                               ? (uint32_t)(((c0 + i) * kOFloats + rt * kD + d0) * sizeof(float))
+                               ? (uint32_t)(((c0 + i) * kOFloats + 4 * tid) * sizeof(float))
                                : 0x80000000u;
       a[i] = __builtin_amdgcn_raw_buffer_load_b128(rp, off, 0, kCoherent);
-      bb[i] = __builtin_amdgcn_raw_buffer_load_b128(rp, off + 16, 0, kCoherent);
+      bb[i] = __builtin_amdgcn_raw_buffer_load_b128(rp, off + 4096, 0, kCoherent);
     }
   };
   // The first batch of outputs and the whole table of maxima and sums are in
@@ -414,6 +417,346 @@ __global__ __launch_bounds__(256, 2) void swa_attention_kernel(
     __hip_atomic_store(&counters[cidx], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+
+// ---- Query heads of one KV head over a shared K/V ring in LDS ----
+//
+// Grouped-query attention: the query heads of a group read the same key and
+// value rows. This kernel gives one workgroup a (sequence, KV head, group of
+// WV query heads, chunk of keys), one wavefront per query head, and fetches
+// every 32-key step's K and V rows once for the whole group, straight into an
+// LDS ring kRing steps deep by buffer loads. One more wavefront only issues
+// those loads: it waits for a step's 16 loads with a constant vmcnt count and
+// meets the others at one barrier per step. The wavefronts that compute issue
+// no memory loads inside the loop, so no wait the compiler places before
+// their LDS reads can stall on the ring. A row's 16-byte pieces are stored
+// XOR-swizzled by the row index, so the K operand reads (16 rows, one piece
+// each) and the transposing V^T reads (16 rows, 8 bytes each) hit distinct
+// banks. Each wavefront keeps its head's online softmax over the whole chunk,
+// so no merge runs between wavefronts; chunks merge through the same partial
+// records as the one-head kernel, with one arrival count per group.
+constexpr int kRing = 2;                          // steps in flight
+constexpr int kRingKeys = 64;                     // keys per step
+constexpr int kRingSlot = 2 * kRingKeys * kRowBytes;   // K rows, then V rows, of one step
+constexpr int kRingLds = kRing * kRingSlot;
+constexpr int kRingMaxChunks = kSwaRingMaxChunks;   // merge table: 128 B per chunk and wavefront
+static_assert(kRingMaxChunks * 8 <= 128, "merge table loads: two 16-byte words per lane");
+static_assert(8 * kRingMaxChunks * 128 <= kRingLds, "merge tables exceed the ring");
+
+// Byte offset of piece p (16 bytes) of row r in a block of swizzled 256-byte rows.
+__device__ __forceinline__ int swz(int r, int p) { return r * kRowBytes + ((p ^ (r & 15)) << 4); }
+
+typedef __attribute__((address_space(3))) void* ring_lds_ptr;
+__device__ __forceinline__ void ring_to_lds(__amdgpu_buffer_rsrc_t r, char* dst, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (ring_lds_ptr)dst, 16, voff, 0, 0, 0);
+}
+
+template <int WV>
+__global__ __launch_bounds__(64 * (WV + 1), 2) void swa_ring_kernel(
+    const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* seq_lens,
+    uint16_t* out, uint32_t* counters, float* partials, int T, int Hq, int Hkv, int S_max,
+    int window, float scale_log2, int chunk, int nchunks, int units) {
+  extern __shared__ __align__(16) char lds[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool loader = wave == WV;                       // the last wavefront fetches
+  const int G = Hq / Hkv;
+  const int NG = G / WV;                                // head groups per KV head
+  const int u = blockIdx.x;
+  if (u >= units) return;
+  const int c = u % nchunks;
+  const int grp = (u / nchunks) % NG;
+  const int kvh = (u / (nchunks * NG)) % Hkv;
+  const int b = u / (nchunks * NG * Hkv);
+  const int h = kvh * G + grp * WV + (loader ? 0 : wave);   // this wavefront's query head
+
+  const int S = min(max(seq_lens[b], T), S_max);
+  const bool full = window == 0 || S <= window;
+  const int half = window >> 1;
+  const int p0 = S - T;
+  const int lo_u = full ? 0 : max(0, p0 - half);
+  const int hi_u = full ? S : min(S, p0 + T + half);
+  const int per = min(chunk, (hi_u - lo_u + nchunks - 1) / nchunks);
+  const int k0 = min(lo_u + c * per, hi_u);
+  const int k1 = min(k0 + per, hi_u);
+  const int nsteps = k1 > k0 ? (k1 - k0 + kRingKeys - 1) / kRingKeys : 0;
+
+  const int tok = lane & 15;
+  const int g = lane >> 4;
+  constexpr float kLazy = 8.0f;
+  float m_run = -INFINITY, l_run = 0.0f;
+  f32x4 o[8];
+#pragma unroll
+  for (int db = 0; db < 8; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (loader) {
+    // Loads of one step: instruction i (0..31) fills rows 4 (i % 16) .. +3 of
+    // K (i < 16) or V; lane L lands at row 4 (i % 16) + L / 16, slot position
+    // L % 16, which holds source piece (L % 16) ^ row. Rows past the sequence
+    // read zeros (steps past the chunk's end fill slots no step reads).
+    const uint32_t kv_seq_bytes = (uint32_t)S * (uint32_t)Hkv * kRowBytes;
+    const __amdgpu_buffer_rsrc_t rk = rsrc(k + (size_t)b * S_max * Hkv * kD, kv_seq_bytes);
+    const __amdgpu_buffer_rsrc_t rv = rsrc(v + (size_t)b * S_max * Hkv * kD, kv_seq_bytes);
+    const uint32_t row_stride = (uint32_t)Hkv * kRowBytes;
+    const int lrow = lane >> 4;
+    const int lpiece = lane & 15;
+    auto issue_step = [&](int st) {
+      char* slot = lds + (st % kRing) * kRingSlot;
+      const int key0 = k0 + kRingKeys * st;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const int row = 4 * (i & 15) + lrow;
+        const uint32_t voff = (uint32_t)(key0 + row) * row_stride + kvh * kRowBytes +
+                              16 * (lpiece ^ (row & 15));
+        ring_to_lds(i < 16 ? rk : rv,
+                    slot + (i < 16 ? 0 : kRingKeys * kRowBytes) + (i & 15) * 1024,
+                    key0 + row < S ? voff : 0x80000000u);
+      }
+    };
+#pragma unroll
+    for (int st = 0; st < kRing - 1; ++st) issue_step(st);
+#pragma unroll 1
+    for (int s = 0; s < nsteps; ++s) {
+      // step s has landed: only the next kRing - 2 steps' loads may be out
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((kRing - 2) * 32) : "memory");
+      issue_step(s + kRing - 1);                     // into the slot step s - 1 used
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  } else {
+    int vlo = 0, vhi = 0;
+    if (tok < T) {
+      const int p = p0 + tok;
+      vlo = max(full ? 0 : max(0, p - half), k0);
+      vhi = min(full ? S : min(S, p + half + 1), k1);
+    }
+    // Keys every query of the block sees: steps inside need no mask (rows
+    // past T score against a zero query and are never stored).
+    const int fast_lo = max(full ? 0 : max(0, p0 + T - 1 - half), k0);
+    const int fast_hi = min(full ? S : min(S, p0 + half + 1), k1);
+    // Q^T operand: query tok, dims 32 j + 8 g .. +7.
+    u32x4 bq[4];
+    {
+      const __amdgpu_buffer_rsrc_t rq = rsrc(q + ((size_t)b * T * Hq + h) * kD,
+                                             (uint32_t)(T * Hq * kRowBytes));
+      const uint32_t qoff = (uint32_t)(tok * Hq * kRowBytes + 16 * g);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bq[j] = ld16(rq, tok < T ? qoff + 64 * j : 0x80000000u);
+    }
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4s* lds_v4s;
+    // V^T reads: rows 4 g + tok / 4 and +16, byte 32 db + 8 (tok % 4) of the row.
+    const int vrow = 4 * g + (tok >> 2);
+    const int vsub = 8 * (tok & 1);
+    const int vpc = (tok & 3) >> 1;
+#pragma unroll 1
+    for (int s = 0; s < nsteps; ++s) {
+      // this wavefront's reads of step s - 1 are done before its slot is refilled
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      const char* slot = lds + (s % kRing) * kRingSlot;
+      const int key0 = k0 + kRingKeys * s;
+      f32x4 acc[4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        acc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const u32x4 kv = *reinterpret_cast<const u32x4*>(slot + swz(16 * kb + tok, 4 * j + g));
+          acc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv),
+                                                            __builtin_bit_cast(bf16x8, bq[j]),
+                                                            acc[kb], 0, 0, 0);
+        }
+      }
+      float sc[4][4];
+      float mx = -INFINITY;
+      if (key0 >= fast_lo && key0 + kRingKeys <= fast_hi) {   // wave-uniform
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            sc[kb][e] = acc[kb][e] * scale_log2;
+            mx = fmaxf(mx, sc[kb][e]);
+          }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int key = key0 + 16 * kb + 4 * g + e;
+            sc[kb][e] = (key >= vlo && key < vhi) ? acc[kb][e] * scale_log2 : -INFINITY;
+            mx = fmaxf(mx, sc[kb][e]);
+          }
+      }
+      mx = xmax(xmax(mx, 16), 32);
+      // The exponent reference moves only when a query's maximum passes it
+      // by more than kLazy (log2 units): probabilities stay at most 2^kLazy,
+      // which the two-part bf16 P carries to the same relative precision.
+      if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazy) != 0) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - (m_new == -INFINITY ? 0.0f : m_new));
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) o[db] *= alpha;
+      }
+      const float ms = m_run == -INFINITY ? 0.0f : m_run;
+      // Each 32-key half: P^T operand from this lane's 8 scores (keys
+      // 16 kb + 4 g + e of its two 16-key blocks), then O^T += V^T P^T.
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        float pv[8];
+        float psum = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          pv[e] = __builtin_amdgcn_exp2f(sc[2 * hh + (e >> 2)][e & 3] - ms);
+          psum += pv[e];
+        }
+        l_run += psum;
+        u32x4 phi, plo;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t hw = pack_bf16x2(pv[2 * w], pv[2 * w + 1]);
+          phi[w] = hw;
+          plo[w] = pack_bf16x2(pv[2 * w] - bf16_bits_to_f32(hw & 0xFFFFu),
+                               pv[2 * w + 1] - bf16_bits_to_f32(hw >> 16));
+        }
+        const char* vs = slot + kRingKeys * kRowBytes;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+          const int pc = 2 * db + vpc;
+          const v4s r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_v4s)(vs + swz(32 * hh + vrow, pc) + vsub));
+          const v4s r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_v4s)(vs + swz(32 * hh + vrow + 16, pc) + vsub));
+          const u32x2 w0 = __builtin_bit_cast(u32x2, r0), w1 = __builtin_bit_cast(u32x2, r1);
+          const u32x4 av = {w0[0], w0[1], w1[0], w1[1]};
+          const f32x4 od = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, phi), o[db], 0, 0, 0);
+          o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, plo), od, 0, 0, 0);
+        }
+      }
+    }
+    l_run += __shfl_xor(l_run, 16);
+    l_run += __shfl_xor(l_run, 32);
+  }
+
+  const size_t pstride = (size_t)nchunks * kPartFloats;
+  const uint32_t ml0 = (uint32_t)(nchunks * kOFloats * sizeof(float));
+  if (nchunks == 1) {
+    if (!loader && tok < T) {
+      const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
+      uint16_t* orow = out + (((size_t)b * T + tok) * Hq + h) * kD + 4 * g;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        u32x2 w;
+        w[0] = pack_bf16x2(o[db][0] * inv, o[db][1] * inv);
+        w[1] = pack_bf16x2(o[db][2] * inv, o[db][3] * inv);
+        *reinterpret_cast<u32x2*>(orow + 16 * db) = w;
+      }
+    }
+    return;
+  }
+
+  // This chunk's record for the head, in the accumulators' own layout:
+  // 16-byte word 64 db + lane holds o[db] of that lane (query lane % 16,
+  // dims 16 db + 4 (lane / 16) .. +3), so every store and every merge load
+  // moves 1 KB of consecutive bytes; then max[16] and sum[16].
+  if (!loader) {
+    const __amdgpu_buffer_rsrc_t rp =
+        rsrc(partials + (size_t)(b * Hq + h) * pstride, (uint32_t)(pstride * sizeof(float)));
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const uint32_t off = (uint32_t)((c * kOFloats + 4 * (64 * db + lane)) * sizeof(float));
+      __builtin_amdgcn_raw_buffer_store_b128(
+          u32x4{__float_as_uint(o[db][0]), __float_as_uint(o[db][1]), __float_as_uint(o[db][2]),
+                __float_as_uint(o[db][3])}, rp, off, 0, kCoherent);
+    }
+    if (g == 0) {
+      const uint32_t moff = ml0 + (uint32_t)((c * 32 + tok) * sizeof(float));
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m_run), rp, moff, 0, kCoherent);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(l_run), rp, moff + 64, 0, kCoherent);
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  __shared__ uint32_t s_last;
+  const int cidx = (b * Hkv + kvh) * NG + grp;
+  if (tid == 0) {
+    const uint32_t prev =
+        __hip_atomic_fetch_add(&counters[cidx], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = prev == (uint32_t)nchunks - 1u ? 1u : 0u;
+  }
+  __syncthreads();
+  if (s_last == 0u) return;
+
+  if (!loader) {
+    // Last arrival: each wavefront merges its head's chunks in chunk order,
+    // every lane the same words it stored. The maxima and sums of all chunks
+    // go to the wavefront's own LDS area; the first batch of words is in
+    // flight with them.
+    const __amdgpu_buffer_rsrc_t rp =
+        rsrc(partials + (size_t)(b * Hq + h) * pstride, (uint32_t)(pstride * sizeof(float)));
+    float* ml = reinterpret_cast<float*>(lds + wave * (kRingMaxChunks * 128));
+    constexpr int kB = 2;                              // chunks per load batch
+    u32x4 a[kB][8];
+    auto issue = [&](int c0) {
+#pragma unroll
+      for (int j = 0; j < kB; ++j)
+#pragma unroll
+        for (int db = 0; db < 8; ++db)
+          a[j][db] = __builtin_amdgcn_raw_buffer_load_b128(
+              rp, c0 + j < nchunks
+                      ? (uint32_t)(((c0 + j) * kOFloats + 4 * (64 * db + lane)) * sizeof(float))
+                      : 0x80000000u,
+              0, kCoherent);
+    };
+    {
+      // nchunks * 8 16-byte words, at most 128: two per lane
+      const u32x4 t0 = __builtin_amdgcn_raw_buffer_load_b128(
+          rp, lane < nchunks * 8 ? ml0 + 16 * lane : 0x80000000u, 0, kCoherent);
+      const u32x4 t1 = __builtin_amdgcn_raw_buffer_load_b128(
+          rp, lane + 64 < nchunks * 8 ? ml0 + 16 * (lane + 64) : 0x80000000u, 0, kCoherent);
+      issue(0);
+      if (lane < nchunks * 8) *reinterpret_cast<u32x4*>(ml + 4 * lane) = t0;
+      if (lane + 64 < nchunks * 8) *reinterpret_cast<u32x4*>(ml + 4 * (lane + 64)) = t1;
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    float Mx = -INFINITY;
+    for (int cc = 0; cc < nchunks; ++cc) Mx = fmaxf(Mx, ml[cc * 32 + tok]);
+    const float Mxs = Mx == -INFINITY ? 0.0f : Mx;
+    f32x4 tot[8];
+#pragma unroll
+    for (int db = 0; db < 8; ++db) tot[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float Lt = 0.0f;
+    for (int c0 = 0; c0 < nchunks; c0 += kB) {
+      if (c0 > 0) issue(c0);
+#pragma unroll
+      for (int j = 0; j < kB; ++j) {
+        const int cc = min(c0 + j, nchunks - 1);
+        const float f = c0 + j < nchunks ? __builtin_amdgcn_exp2f(ml[cc * 32 + tok] - Mxs) : 0.0f;
+        Lt += f * ml[cc * 32 + 16 + tok];
+#pragma unroll
+        for (int db = 0; db < 8; ++db)
+#pragma unroll
+          for (int x = 0; x < 4; ++x) tot[db][x] += f * __uint_as_float(a[j][db][x]);
+      }
+    }
+    if (tok < T) {
+      const float inv = Lt > 0.0f ? 1.0f / Lt : 0.0f;
+      uint16_t* orow = out + (((size_t)b * T + tok) * Hq + h) * kD + 4 * g;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        u32x2 w;
+        w[0] = pack_bf16x2(tot[db][0] * inv, tot[db][1] * inv);
+        w[1] = pack_bf16x2(tot[db][2] * inv, tot[db][3] * inv);
+        *reinterpret_cast<u32x2*>(orow + 16 * db) = w;
+      }
+    }
+  }
+  if (tid == 0)   // ready for the next call on this workspace
+    __hip_atomic_store(&counters[cidx], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 }  // namespace
 
 hipError_t launch_swa_attention(const SwaPlan& p, const void* q, const void* k, const void* v,
@@ -427,6 +770,26 @@ hipError_t launch_swa_attention(const SwaPlan& p, const void* q, const void* k, 
     partials = reinterpret_cast<float*>(static_cast<char*>(ws) + kCounterBytes);
   }
   const float scale_log2 = (float)((double)scale * 1.4426950408889634);
+  if (p.ring > 0) {
+    void (*rk)(const uint16_t*, const uint16_t*, const uint16_t*, const int32_t*, uint16_t*,
+               uint32_t*, float*, int, int, int, int, int, float, int, int, int) = nullptr;
+    switch (p.ring) {
+      case 2: rk = swa_ring_kernel<2>; break;
+      case 3: rk = swa_ring_kernel<3>; break;
+      case 4: rk = swa_ring_kernel<4>; break;
+      case 5: rk = swa_ring_kernel<5>; break;
+      case 6: rk = swa_ring_kernel<6>; break;
+      case 8: rk = swa_ring_kernel<8>; break;
+      default: return hipErrorInvalidValue;
+    }
+    if (p.nchunks > kRingMaxChunks) return hipErrorInvalidValue;
+    rk<<<p.grid, 64 * (p.ring + 1), kRingLds, st>>>(
+        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+        static_cast<const uint16_t*>(v), seq_lens, static_cast<uint16_t*>(out), counters,
+        partials, (int)T, (int)Hq, (int)Hkv, (int)S_max, p.window, scale_log2, p.chunk,
+        p.nchunks, p.units);
+    return hipGetLastError();
+  }
   auto kernel = p.q_lds ? swa_attention_kernel<true> : swa_attention_kernel<false>;
   kernel<<<p.grid, 64 * kWaves, kWavesLds + (p.q_lds ? kQLds : 0), st>>>(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),

@@ -192,9 +192,9 @@ def test_grouped_entry_points_validate():
 
 
 def _swa(L, B=1, T=16, Hq=20, Hkv=4, D=128, S_max=8208, window=1024, scale=0.088, chunk=0,
-         q=FAKE, k=FAKE, v=FAKE, lens=FAKE, out=FAKE, ws=FAKE, ws_bytes=1 << 30):
-    return L.qg_swa_attention_chunk(q, k, v, lens, out, B, T, Hq, Hkv, D, S_max, window, scale,
-                                    chunk, ws, ws_bytes, None)
+         heads=0, q=FAKE, k=FAKE, v=FAKE, lens=FAKE, out=FAKE, ws=FAKE, ws_bytes=1 << 30):
+    return L.qg_swa_attention_plan(q, k, v, lens, out, B, T, Hq, Hkv, D, S_max, window, scale,
+                                   chunk, heads, ws, ws_bytes, None)
 
 
 def test_swa_attention_validates():
@@ -208,6 +208,14 @@ def test_swa_attention_validates():
     assert _swa(L, S_max=8) == SHAPE                # shorter than the block
     assert _swa(L, window=-1) == SHAPE
     assert _swa(L, chunk=48) == SHAPE               # not a multiple of 32
+    # query heads per workgroup: 2-6 or 8, dividing Hq / Hkv (5 here)
+    for heads in (-1, 7, 9, 2, 3, 4, 6, 8):
+        assert _swa(L, heads=heads) == SHAPE, heads
+    assert _swa(L, Hq=24, Hkv=4, heads=4) == SHAPE  # 6 heads per KV head
+    # the shared-ring kernel merges at most 16 chunks
+    assert _swa(L, window=0, heads=5, chunk=512) == SHAPE      # 17 chunks
+    assert L.qg_swa_workspace_bytes_plan(1, 16, 20, 4, 128, 8208, 0, 512, 5) == 0
+    assert L.qg_swa_workspace_bytes_plan(1, 16, 20, 4, 128, 8208, 0, 512, 1) > 0   # one head each
     assert _swa(L, B=-1) == SHAPE
     assert _swa(L, S_max=1 << 22, Hkv=16) == SHAPE  # a sequence's cache past 2^31 bytes
     assert _swa(L, scale=float("nan")) == SHAPE
@@ -231,11 +239,22 @@ def test_swa_workspace_sizes():
     L = q.lib()
     # one chunk (a short cache, or a chunk covering the whole window) needs none
     assert L.qg_swa_workspace_bytes(1, 16, 20, 4, 128, 100, 0) == 0
-    assert L.qg_swa_workspace_bytes_chunk(1, 16, 20, 4, 128, 8208, 1024, 2048) == 0
+    assert L.qg_swa_workspace_bytes_plan(1, 16, 20, 4, 128, 8208, 1024, 2048, 0) == 0
+    assert L.qg_swa_workspace_bytes_plan(1, 16, 20, 4, 128, 8208, 1024, 2048, 5) == 0
     # otherwise the counter block plus per-chunk partials (16 x 128 outputs,
     # 16 maxima, 16 sums, fp32) for each (sequence, query head)
-    n = L.qg_swa_workspace_bytes_chunk(2, 16, 8, 2, 128, 1000, 0, 256)
+    n = L.qg_swa_workspace_bytes_plan(2, 16, 8, 2, 128, 1000, 0, 256, 0)
     assert n == 65536 + 2 * 8 * 4 * (16 * 128 + 32) * 4
+    # the shared-ring kernel keeps the same record per (sequence, query head, chunk)
+    assert L.qg_swa_workspace_bytes_plan(2, 16, 8, 2, 128, 1000, 0, 256, 2) == n
+    assert L.qg_swa_workspace_bytes_plan(2, 16, 8, 2, 128, 1000, 0, 256, 3) == 0   # 3 does not divide 4
+    # the library's own split: batch 8 of the drafter's heads over the full
+    # 8,208-token cache streams K/V once per 5 query heads in 8 chunks; batch
+    # 1 and windowed spans keep one head per workgroup (6 and 5 chunks here)
+    rec = (16 * 128 + 32) * 4
+    assert L.qg_swa_workspace_bytes(8, 16, 20, 4, 128, 8208, 0) == 65536 + 8 * 20 * 8 * rec
+    assert L.qg_swa_workspace_bytes(1, 16, 20, 4, 128, 8208, 0) == 65536 + 20 * 12 * rec
+    assert L.qg_swa_workspace_bytes(1, 16, 20, 4, 128, 8208, 1024) == 65536 + 20 * 5 * rec
     # a window wider than the cache is no window
     assert L.qg_swa_workspace_bytes(1, 16, 20, 4, 128, 1000, 5000) == \
         L.qg_swa_workspace_bytes(1, 16, 20, 4, 128, 1000, 0)

@@ -31,8 +31,8 @@ pytestmark = pytest.mark.gpu
 D = 128
 
 
-def _run(B, T, Hq, Hkv, S_max, lens, window, seed, scale=None, chunk=0, std=1.0, poison=False,
-         ws=None):
+def _run(B, T, Hq, Hkv, S_max, lens, window, seed, scale=None, chunk=0, heads=0, std=1.0,
+         poison=False, ws=None):
     qb, kb, vb = workloads.attention_inputs(B, T, Hq, Hkv, D, S_max, seed, std=std)
     if poison:   # NaN past each sequence's end: must never be read
         for b, S in enumerate(lens):
@@ -40,11 +40,11 @@ def _run(B, T, Hq, Hkv, S_max, lens, window, seed, scale=None, chunk=0, std=1.0,
             vb[b, min(max(S, T), S_max):] = 0x7FC0
     sc = 1.0 / np.sqrt(D) if scale is None else scale
     out = Guarded((B, T, Hq, D), torch.bfloat16)
-    wsg = ws or GuardedWorkspace(q.lib().qg_swa_workspace_bytes_chunk(B, T, Hq, Hkv, D, S_max,
-                                                                       window, chunk))
+    wsg = ws or GuardedWorkspace(q.lib().qg_swa_workspace_bytes_plan(B, T, Hq, Hkv, D, S_max,
+                                                                      window, chunk, heads))
     q.swa_attention(dev_bf16(qb), dev_bf16(kb), dev_bf16(vb),
                     torch.tensor(lens, dtype=torch.int32, device=DEV), window, sc,
-                    chunk=chunk, out=out.t, ws=wsg.t)
+                    chunk=chunk, heads=heads, out=out.t, ws=wsg.t)
     got = out.check("attention")
     wsg.check("attention")
     return qb, kb, vb, sc, host_u16(got)
@@ -87,8 +87,9 @@ def test_drafter_long_context_full_size(window):
 @pytest.mark.parametrize("window", [1024, 2048, 0])
 def test_batch8_long_context_plans(window):
     # eight sequences of the drafter's heads over the Long cache, ragged: the
-    # library's plan runs windowed spans unsplit at 160 query heads and
-    # splits the full cache in three (every chunk count the batch-8 rows use)
+    # library's plan runs windowed spans unsplit at 160 query heads, one head
+    # per workgroup, and the full cache in eight chunks with the 5 query heads
+    # of a KV head sharing one stream of its rows
     A = workloads.ATTENTION
     S = A["context"] + A["T"]
     lens = [S, 5000, 1000, 600, S, 3000, 100, 2048]
@@ -139,7 +140,7 @@ def test_scales_and_sharp_softmax(scale, std):
 def test_deterministic_and_workspace_reusable():
     lens = [2500, 1800]
     a = _parity(2, 16, 20, 4, 2500, lens, 0, 6800)
-    ws = GuardedWorkspace(q.lib().qg_swa_workspace_bytes_chunk(2, 16, 20, 4, D, 2500, 0, 0))
+    ws = GuardedWorkspace(q.lib().qg_swa_workspace_bytes_plan(2, 16, 20, 4, D, 2500, 0, 0, 0))
     for _ in range(3):     # one workspace reused: its counters are left at zero
         _, _, _, _, b = _run(2, 16, 20, 4, 2500, lens, 0, 6800, ws=ws)
         np.testing.assert_array_equal(a, b)
@@ -163,3 +164,56 @@ def test_empty_batch_is_a_no_op():
     lens = torch.empty((0,), dtype=torch.int32, device=DEV)
     out = q.swa_attention(qt, kt, kt, lens, 0)
     assert out.shape == qt.shape
+
+
+# ---- query heads of one KV head sharing one stream of its K/V rows ----
+
+@pytest.mark.parametrize("heads,Hq,Hkv", [(2, 8, 2), (3, 6, 1), (4, 16, 2), (5, 20, 4), (6, 12, 2),
+                                          (8, 8, 1)])
+def test_shared_stream_head_counts(heads, Hq, Hkv):
+    # every head count the kernel is built for, with two head groups per KV
+    # head where Hq / Hkv allows, ragged lengths and a chunk that ends inside
+    # a 64-key step
+    _parity(3, 16, Hq, Hkv, 2100, [2100, 1333, 40], 0, 7100 + heads, chunk=416, heads=heads)
+
+
+@pytest.mark.parametrize("window,chunk", [(1024, 96), (64, 32), (1, 32)])
+def test_shared_stream_windows(window, chunk):
+    _parity(2, 16, 20, 4, 3000, [3000, 1100], window, 7200 + window, chunk=chunk, heads=5)
+
+
+@pytest.mark.parametrize("T", [1, 7])
+def test_shared_stream_partial_blocks(T):
+    _parity(2, T, 20, 4, 1500, [1500, 700], 0, 7300 + T, chunk=256, heads=5)
+
+
+def test_shared_stream_one_chunk():
+    # a chunk covering the whole span: no merge, outputs stored directly
+    _parity(2, 16, 20, 4, 1000, [1000, 517], 0, 7400, chunk=1024, heads=5)
+
+
+def test_shared_stream_most_chunks():
+    # 16 chunks (the most this kernel merges), several of them past the end
+    # of the shorter sequences
+    _parity(3, 16, 20, 4, 4096, [4096, 900, 16], 0, 7500, chunk=256, heads=5)
+
+
+def test_shared_stream_cache_past_sequence_end_is_not_read():
+    lens = [900, 417, 16]
+    _, _, _, _, clean = _run(3, 16, 20, 4, 1000, lens, 0, 7600, chunk=128, heads=5)
+    _, _, _, _, dirty = _run(3, 16, 20, 4, 1000, lens, 0, 7600, chunk=128, heads=5, poison=True)
+    np.testing.assert_array_equal(dirty, clean)
+
+
+def test_shared_stream_deterministic_and_workspace_shared():
+    # one workspace serves both kernels in turn: each leaves its arrival
+    # counters at zero
+    lens = [2500, 1800]
+    need = max(q.lib().qg_swa_workspace_bytes_plan(2, 16, 20, 4, D, 2500, 0, 320, h)
+               for h in (1, 5))
+    ws = GuardedWorkspace(need)
+    a = _parity(2, 16, 20, 4, 2500, lens, 0, 7700, chunk=320, heads=5, ws=ws)
+    for h in (1, 5, 5, 1, 5):
+        _, _, _, _, b = _run(2, 16, 20, 4, 2500, lens, 0, 7700, chunk=320, heads=h, ws=ws)
+        if h == 5:
+            np.testing.assert_array_equal(a, b)
