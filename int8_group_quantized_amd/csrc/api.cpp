@@ -185,6 +185,7 @@ qg_status grouped_plan(int bits, int64_t M, int64_t K, const qg_group_item* item
   qg::small_plan_group(*plan, g);
   if (plan->splits > 1 && (int64_t)g->wg_total * plan->row_blocks > kMaxCounters)
     return QG_ERR_SHAPE;
+  if (!qg::small_plan_partials_fit(*plan, g->n_total)) return QG_ERR_SHAPE;
   return QG_OK;
 }
 

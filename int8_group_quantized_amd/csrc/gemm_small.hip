@@ -53,12 +53,13 @@ namespace qg {
 namespace {
 
 
-// Device-coherent (agent scope) accesses for the split-K partials.
-__device__ __forceinline__ void store_coherent(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_coherent(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Device-coherent (agent scope: sc1, past the per-XCD L2) 16-byte accesses
+// for the split-K partials, through a buffer resource whose range check turns
+// an offset at or past 2^31 into a zero read.
+constexpr int kCoherent = 16;
+constexpr uint32_t kNoRead = 0x80000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t part_rsrc(float* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(p, 0, (int)bytes, 0x00020000);
 }
 
 // The INT4 expansion constant held in a vector register the optimiser cannot
@@ -389,19 +390,27 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_small_kernel(
     return;
   }
 
+  // Partials in the accumulators' own lane order: 16-byte word
+  // ((split * row blocks + row block) * NBT + column block) * 64 + lane holds
+  // this lane's acc (column l16, rows 4 lq .. +3 of the 16-row block; NBT =
+  // column blocks of all GEMMs of the call), so every store and every merge
+  // load of a wavefront moves 1 KB of consecutive bytes.
+  const uint32_t nbt = (uint32_t)ga.n_total >> 4;
+  const uint32_t split_bytes = gridDim.z * nbt * 1024u;
+  const __amdgpu_buffer_rsrc_t rp = part_rsrc(partials, splits * split_bytes);
+  uint32_t poff[NBW];
+#pragma unroll
+  for (int c = 0; c < NBW; ++c)
+    poff[c] = ((blockIdx.z * nbt + (uint32_t)(colp >> 4) + (uint32_t)(cb0 + (c < nvalid ? c : 0))) *
+                   64u + (uint32_t)lane) * 16u;
   if (wk == 0) {
 #pragma unroll
     for (int c = 0; c < NBW; ++c) {
-      if (c < nvalid) {
-        const int n = (cb0 + c) * 16 + l16;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * lq + e;
-          if (r < mrows)
-            store_coherent(&partials[((int64_t)split * M + row0 + r) * ga.n_total + colp + n],
-                           acc[c][e]);
-        }
-      }
+      if (c < nvalid)
+        __builtin_amdgcn_raw_buffer_store_b128(
+            u32x4{__float_as_uint(acc[c][0]), __float_as_uint(acc[c][1]),
+                  __float_as_uint(acc[c][2]), __float_as_uint(acc[c][3])},
+            rp, poff[c] + split * split_bytes, 0, kCoherent);
     }
   }
   // The coherent stores must have completed before the arrival is counted.
@@ -425,47 +434,36 @@ __global__ __launch_bounds__(64 * WN * WK, 2) void gemm_small_kernel(
     // four, since the larger merge's registers slowed the M = 1 gate/up
     // kernel, which shares the instantiation, by 13%.
     constexpr int U = (NBW == 1) ? 8 : 4;
-    const int64_t sstride = (int64_t)M * ga.n_total;
-    const float* pp[NBW][4];
-    bool ok[NBW][4];
-    float sum[NBW][4];
+    f32x4 sum[NBW];
 #pragma unroll
-    for (int c = 0; c < NBW; ++c) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * lq + e;
-        ok[c][e] = c < nvalid && r < mrows;
-        pp[c][e] = partials + (int64_t)(row0 + (ok[c][e] ? r : 0)) * ga.n_total + colp +
-                   (ok[c][e] ? (cb0 + c) * 16 + l16 : 0);
-        sum[c][e] = 0.0f;
-      }
-    }
+    for (int c = 0; c < NBW; ++c) sum[c] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int sp0 = 0; sp0 < splits; sp0 += U) {
-      float v[U][NBW][4];
+      u32x4 v[U][NBW];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const bool in = sp0 + u < splits;
 #pragma unroll
-        for (int c = 0; c < NBW; ++c) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            v[u][c][e] = (in && ok[c][e]) ? load_coherent(pp[c][e] + (sp0 + u) * sstride) : 0.0f;
-        }
+        for (int c = 0; c < NBW; ++c)
+          v[u][c] = __builtin_amdgcn_raw_buffer_load_b128(
+              rp, (sp0 + u < splits && c < nvalid) ? poff[c] + (sp0 + u) * split_bytes : kNoRead,
+              0, kCoherent);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
 #pragma unroll
         for (int c = 0; c < NBW; ++c) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) sum[c][e] += v[u][c][e];
+          for (int e = 0; e < 4; ++e) sum[c][e] += __uint_as_float(v[u][c][e]);
         }
       }
     }
 #pragma unroll
     for (int c = 0; c < NBW; ++c) {
+      if (c < nvalid) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (ok[c][e]) out[(int64_t)(row0 + 4 * lq + e) * N + (cb0 + c) * 16 + l16] = A::out(sum[c][e]);
+        for (int e = 0; e < 4; ++e)
+          if (4 * lq + e < mrows)
+            out[(int64_t)(row0 + 4 * lq + e) * N + (cb0 + c) * 16 + l16] = A::out(sum[c][e]);
+      }
     }
   }
   if (tid == 0)   // ready for the next call on this workspace

@@ -96,14 +96,23 @@ bool make_small_plan(int bits, int64_t M, int64_t K, int64_t N, int nbw, int wk,
   p.sg = p.gps;
   if (p.splits > 65535 || p.row_blocks > 65535) return false;
   if (p.splits > 1 && (int64_t)p.wgs_n * p.row_blocks > kMaxCounters) return false;
+  if (!small_plan_partials_fit(p, N)) return false;
   if ((int64_t)small_plan_lds_bytes(p, M) > kLdsMax) return false;
   *plan = p;
   return true;
 }
 
 size_t small_plan_workspace(const SmallPlan& p, int64_t M, int64_t N) {
+  (void)M;
   if (p.splits <= 1) return 0;
-  return (size_t)kCounterBytes + (size_t)p.splits * (size_t)M * (size_t)N * sizeof(float);
+  // Every split keeps whole 16-row blocks (the accumulators' lane order).
+  return (size_t)kCounterBytes +
+         (size_t)p.splits * (size_t)p.row_blocks * 16 * (size_t)N * sizeof(float);
+}
+
+bool small_plan_partials_fit(const SmallPlan& p, int64_t n_total) {
+  // The split partials are addressed with 32-bit byte offsets below 2^31.
+  return p.splits <= 1 || (int64_t)p.splits * p.row_blocks * 16 * n_total * 4 < (int64_t(1) << 31);
 }
 
 void small_plan_group(const SmallPlan& p, GroupArgs* g) {

@@ -81,6 +81,9 @@ hipError_t launch_gemm_prefill(int bits, const PrefillPlan& p, const void* x, bo
 bool make_small_plan(int bits, int64_t M, int64_t K, int64_t N, int nbw, int wk,
                      int splits, SmallPlan* plan);
 size_t small_plan_workspace(const SmallPlan& p, int64_t M, int64_t N);
+// False when the split partials of a plan over n_total columns would pass
+// 2^31 bytes.
+bool small_plan_partials_fit(const SmallPlan& p, int64_t n_total);
 size_t small_plan_lds_bytes(const SmallPlan& p, int64_t M);
 
 hipError_t launch_rtn_scales(int bits, const void* W, bool w_bf16, int64_t K,

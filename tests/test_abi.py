@@ -57,9 +57,11 @@ def test_sizes():
     assert L.qg_packed_bytes(3, 128, 16) == 0
     assert L.qg_scale_bytes(9728, 2560) == 76 * 2560 * 2
     assert L.qg_workspace_bytes(4, 0, 128, 16) == 0
-    # a split-K plan needs the counter block plus fp32 partials
+    # a split-K plan needs the counter block plus fp32 partials: whole 16-row
+    # blocks per split
     ws = L.qg_workspace_bytes_plan(4, 3, 1024, 64, 1, 1, 4)
-    assert ws == 65536 + 4 * 3 * 64 * 4
+    assert ws == 65536 + 4 * 16 * 64 * 4
+    assert L.qg_workspace_bytes_plan(4, 17, 1024, 64, 1, 1, 4) == 65536 + 4 * 32 * 64 * 4
     assert L.qg_workspace_bytes_plan(4, 3, 1024, 64, 1, 1, 1) == 0
     assert L.qg_workspace_bytes_plan(4, 3, 1024, 64, 3, 1, 1) == 0   # bad plan -> 0
     # the library's own plans: the decode GEMV and the 2-16-row GEMV (at most
