@@ -216,16 +216,17 @@ bool make_swa_plan(int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t S_max,
     ring = heads_req;
   } else if (heads_req == 0 && chunk_req == 0) {
     // The shared-ring kernel reads each K/V row once for up to eight query
-    // heads; it pays off on long spans once the (sequence, KV head, head
-    // group) count fills the GPU at about eight chunks each (MI355X, the
-    // drafter's Long-context shapes: batch 8, 20 query over 4 KV heads, full
-    // attention over 8,208 keys: 38 us against 67 us for one head per
-    // workgroup; windowed spans and batch 1 stay faster one head each).
+    // heads; it pays off on long spans once there are 16 or more (sequence,
+    // KV head, head group) units to split into chunks (MI355X, 20 query over
+    // 4 KV heads, full attention over 8,208 keys: batch 4 30 us against 39
+    // us for one head per workgroup, batch 8 38 against 67, batch 16 63
+    // against 173, batch 32 114 against 278; batch 2 equal, windowed spans
+    // and batch 1 faster one head each).
     int64_t h = 0;
     for (int64_t c : {8, 6, 5, 4, 3, 2})
       if (h == 0 && ring_ok(c)) h = c;
     const int64_t groups = h > 0 ? B * Hkv * (G / h) : 0;
-    if (h > 0 && typ >= 4096 && groups >= 32 && groups <= 256) ring = h;
+    if (h > 0 && typ >= 4096 && groups >= 16 && groups <= 256) ring = h;
   }
   int64_t n = 1;
   if (ring > 0) {

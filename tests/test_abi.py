@@ -250,11 +250,13 @@ def test_swa_workspace_sizes():
     # the shared-ring kernel keeps the same record per (sequence, query head, chunk)
     assert L.qg_swa_workspace_bytes_plan(2, 16, 8, 2, 128, 1000, 0, 256, 2) == n
     assert L.qg_swa_workspace_bytes_plan(2, 16, 8, 2, 128, 1000, 0, 256, 3) == 0   # 3 does not divide 4
-    # the library's own split: batch 8 of the drafter's heads over the full
-    # 8,208-token cache streams K/V once per 5 query heads in 8 chunks; batch
-    # 1 and windowed spans keep one head per workgroup (6 and 5 chunks here)
+    # the library's own split: batch 4 and 8 of the drafter's heads over the
+    # full 8,208-token cache stream K/V once per 5 query heads in 16 and 8
+    # chunks; batch 1 and windowed spans keep one head per workgroup (12 and
+    # 5 chunks here)
     rec = (16 * 128 + 32) * 4
     assert L.qg_swa_workspace_bytes(8, 16, 20, 4, 128, 8208, 0) == 65536 + 8 * 20 * 8 * rec
+    assert L.qg_swa_workspace_bytes(4, 16, 20, 4, 128, 8208, 0) == 65536 + 4 * 20 * 16 * rec
     assert L.qg_swa_workspace_bytes(1, 16, 20, 4, 128, 8208, 0) == 65536 + 20 * 12 * rec
     assert L.qg_swa_workspace_bytes(1, 16, 20, 4, 128, 8208, 1024) == 65536 + 20 * 5 * rec
     # a window wider than the cache is no window

@@ -96,6 +96,15 @@ def test_batch8_long_context_plans(window):
     _parity(8, A["T"], A["Hq"], A["Hkv"], S, lens, window, 6050 + window)
 
 
+def test_batch4_full_cache_plan():
+    # four sequences over the Long cache without a window: the library's plan
+    # streams K/V once per KV head group in 16 chunks; one sequence is only
+    # the block, one ends inside the first chunk
+    A = workloads.ATTENTION
+    S = A["context"] + A["T"]
+    _parity(4, A["T"], A["Hq"], A["Hkv"], S, [S, 4100, 700, 16], 0, 6080)
+
+
 @pytest.mark.parametrize("window", [0, 64, 256, 1024, 5, 1])
 def test_ragged_batch(window):
     # a long sequence, a medium one, one that is only the block, and one
