@@ -13,7 +13,9 @@
 // Work split. A workgroup owns one (sequence, query head, chunk of keys); its
 // four wavefronts take 32-key steps of the chunk in turn and keep an online
 // softmax each. Query heads that share a KV head are dealt to the same XCD
-// (workgroup i runs on XCD i % 8), so their K/V rows come from one L2.
+// (workgroup i runs on XCD i % 8), so their K/V rows come from one L2. For
+// long spans with many sequences a second kernel (below) gives one workgroup
+// all query heads of a KV head over a single stream of its K/V rows.
 //
 // Both products run on the bf16 matrix core (16x16x32), transposed so that
 // no probability ever leaves the registers:
@@ -423,17 +425,18 @@ __global__ __launch_bounds__(256, 2) void swa_attention_kernel(
 // Grouped-query attention: the query heads of a group read the same key and
 // value rows. This kernel gives one workgroup a (sequence, KV head, group of
 // WV query heads, chunk of keys), one wavefront per query head, and fetches
-// every 32-key step's K and V rows once for the whole group, straight into an
-// LDS ring kRing steps deep by buffer loads. One more wavefront only issues
-// those loads: it waits for a step's 16 loads with a constant vmcnt count and
-// meets the others at one barrier per step. The wavefronts that compute issue
+// every 64-key step's K and V rows (32 KB) once for the whole group, straight
+// into an LDS ring kRing steps deep by buffer loads. One more wavefront only
+// issues those loads (32 per step, 1 KB each): it waits for a step with a
+// constant vmcnt count and meets the others at one barrier per step. The wavefronts that compute issue
 // no memory loads inside the loop, so no wait the compiler places before
 // their LDS reads can stall on the ring. A row's 16-byte pieces are stored
 // XOR-swizzled by the row index, so the K operand reads (16 rows, one piece
 // each) and the transposing V^T reads (16 rows, 8 bytes each) hit distinct
 // banks. Each wavefront keeps its head's online softmax over the whole chunk,
-// so no merge runs between wavefronts; chunks merge through the same partial
-// records as the one-head kernel, with one arrival count per group.
+// so no merge runs between wavefronts; chunks merge through partial records
+// of the one-head kernel's size (O, maxima, sums per chunk and head, here in
+// the accumulators' lane order), with one arrival count per head group.
 constexpr int kRing = 2;                          // steps in flight
 constexpr int kRingKeys = 64;                     // keys per step
 constexpr int kRingSlot = 2 * kRingKeys * kRowBytes;   // K rows, then V rows, of one step
