@@ -85,12 +85,17 @@ def test_small_shapes_every_plan(bits, M, K, N):
 @pytest.mark.parametrize("M", [17, 33, 64])
 def test_multi_row_blocks(bits, M):
     """M > 16: the library's plan (prefill kernel) and the small-M kernel
-    over 16-row blocks (explicit plan) both match the oracle."""
+    over 16-row blocks (explicit plans, K unsplit and split across
+    workgroups, whose partials are kept per row block) all match the
+    oracle; a split plan repeats bit for bit."""
     K, N = 512, 96
     x, c, s = _inputs(bits, M, K, N, 900 + M)
     ref = gemm.gemm_ref(x, c, s, SDT[bits])
     _assert_close(_run(bits, x, c, s, N), ref, "M=%d prefill" % M)
-    _assert_close(_run(bits, x, c, s, N, plan=(1, 1, 1)), ref, "M=%d row blocks" % M)
+    for plan in [(1, 1, 1), (1, 1, 4), (2, 4, 2), (4, 1, 3)]:
+        _assert_close(_run(bits, x, c, s, N, plan=plan), ref, "M=%d row blocks %s" % (M, plan))
+    a = _run(bits, x, c, s, N, plan=(1, 1, 4))
+    assert np.array_equal(a, _run(bits, x, c, s, N, plan=(1, 1, 4)))
 
 
 @pytest.mark.parametrize("bits", [4, 8])
