@@ -95,8 +95,9 @@ size_t qg_scale_bytes(int64_t K, int64_t N);
  * 65536 bytes of a workspace hold arrival counters: they must
  * be zero before the first call that uses the workspace, and every completed
  * call leaves them zero again. The rest holds fp32 split-K partial sums
- * (M <= 16) or, for INT4 with M > 16, the per-row, per-group activation sums
- * that remove the code offset; it needs no initial value. Calls that share
+ * (the small-M kernel: M <= 16, or any M under an explicit plan) or, for
+ * INT4 with M > 16 on the library's plan, the per-row, per-group activation
+ * sums that remove the code offset; it needs no initial value. Calls that share
  * one workspace must not overlap in time (use one stream or distinct
  * workspaces). The same sizes apply to the fp16-activation entry points. */
 size_t qg_workspace_bytes(int bits, int64_t M, int64_t K, int64_t N);
