@@ -164,8 +164,10 @@ qg_status qgemm_w8a16(const void* x, const void* packed_w, const void* scales,
 /* The same GEMMs with an explicit tiling plan, for tests and tuning.
  *   cols_per_wave  16-column blocks per wavefront: 1, 2 or 4
  *   k_waves        wavefronts of a workgroup that split K: 1, 2, 4 or 8 with
- *                  cols_per_wave 1; 1 or 4 with cols_per_wave 2 or 4. A
- *                  workgroup has 4 wavefronts, or 8 when k_waves is 8
+ *                  cols_per_wave 1; 1, 2 or 4 with cols_per_wave 2; 1 or 4
+ *                  with cols_per_wave 4. A workgroup has 4 wavefronts, 6
+ *                  (three along N) for cols_per_wave 2 with k_waves 2, or 8
+ *                  when k_waves is 8
  *   splits         workgroups that split K (>= 1, at most K/128)
  * Any argument 0 takes the library's choice. Unsupported values give
  * QG_ERR_PLAN. workspace must cover qg_workspace_bytes_plan(). */

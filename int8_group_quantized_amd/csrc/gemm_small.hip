@@ -497,7 +497,7 @@ hipError_t launch_shape(const SmallPlan& p, const void* x, const GroupArgs& g, b
 #define QG_G(NBW, WN, WK)                                                                    \
     if (p.nbw == NBW && p.wn == WN && p.wk == WK)                                            \
       return launch_variant<BITS, SBF, XH, true, MR, NBW, WN, WK>(p, x, g, s_cbm, M, K, ws, st);
-    QG_G(1, 1, 4) QG_G(2, 1, 4) QG_G(2, 4, 1) QG_G(1, 4, 1)
+    QG_G(1, 1, 4) QG_G(2, 1, 4) QG_G(2, 4, 1) QG_G(2, 3, 2) QG_G(1, 4, 1)
 #undef QG_G
     return hipErrorInvalidValue;
   }
@@ -505,7 +505,7 @@ hipError_t launch_shape(const SmallPlan& p, const void* x, const GroupArgs& g, b
   if (p.nbw == NBW && p.wn == WN && p.wk == WK)                                              \
     return launch_variant<BITS, SBF, XH, false, MR, NBW, WN, WK>(p, x, g, s_cbm, M, K, ws, st);
   QG_V(1, 4, 1) QG_V(1, 2, 2) QG_V(1, 1, 4) QG_V(1, 1, 8)
-  QG_V(2, 4, 1) QG_V(2, 1, 4)
+  QG_V(2, 4, 1) QG_V(2, 3, 2) QG_V(2, 1, 4)
   QG_V(4, 4, 1) QG_V(4, 1, 4)
 #undef QG_V
   return hipErrorInvalidValue;

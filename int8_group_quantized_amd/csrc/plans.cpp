@@ -18,7 +18,7 @@ constexpr int kCUs = 256;                   // MI355X compute units (plan heuris
 // waves along K).
 bool shape_supported(int nbw, int wn, int wk) {
   static const int ok[][3] = {{1, 4, 1}, {1, 2, 2}, {1, 1, 4}, {1, 1, 8},
-                              {2, 4, 1}, {2, 1, 4}, {4, 4, 1}, {4, 1, 4}};
+                              {2, 4, 1}, {2, 3, 2}, {2, 1, 4}, {4, 4, 1}, {4, 1, 4}};
   for (const auto& s : ok)
     if (s[0] == nbw && s[1] == wn && s[2] == wk) return true;
   return false;
@@ -56,8 +56,11 @@ bool make_small_plan(int bits, int64_t M, int64_t K, int64_t N, int nbw, int wk,
     // staged x group between eight column blocks (two per wavefront), long K
     // splits across workgroups of four column blocks (about 16 INT4 or 13
     // INT8 groups each), and the rest use four K-wavefronts per column block.
+    // Wide INT4 shapes instead take six column blocks over six wavefronts,
+    // two along K (K = 2560, N = 19456: 9.8 against 10.25 us; INT8 13.7
+    // against 13.0, so INT8 keeps eight blocks along N).
     if (NB >= 1024) {
-      nbw = 2; wk = 1; splits = 1;
+      nbw = 2; wk = (bits == 4) ? 2 : 1; splits = 1;
     } else if (G >= 40) {
       const int per = bits == 4 ? 16 : 13;
       nbw = 1; wk = 1; splits = (int)((G + per - 1) / per);
@@ -71,7 +74,7 @@ bool make_small_plan(int bits, int64_t M, int64_t K, int64_t N, int nbw, int wk,
     // waves that split K inside a workgroup.
     wk = (NB >= 1024) ? 1 : (NB >= 128 ? 4 : 8);
   }
-  const int wn = (wk >= 8) ? 1 : ((nbw >= 2 && wk == 4) ? 1 : 4 / wk);
+  const int wn = (wk >= 8) ? 1 : ((nbw >= 2 && wk == 4) ? 1 : ((nbw == 2 && wk == 2) ? 3 : 4 / wk));
   if (!shape_supported(nbw, wn, wk)) return false;
   p.nbw = nbw;
   p.wk = wk;

@@ -57,7 +57,7 @@ def _assert_close(got, ref, what=""):
 
 
 PLANS = [None, (1, 1, 1), (1, 4, 1), (2, 4, 3), (4, 1, 2), (4, 4, 5), (1, 2, 7), (2, 1, 2),
-         (1, 8, 2)]
+         (1, 8, 2), (2, 2, 1), (2, 2, 3)]
 SHAPES = [(1, 256, 512), (3, 896, 592), (16, 1280, 272), (7, 384, 48), (16, 128, 16)]
 
 
@@ -242,7 +242,7 @@ def test_workspace_reuse_across_plans():
     ws = torch.zeros(1 << 20, dtype=torch.uint8, device="cuda:0")
     pg = q.prepack(dev_i8(c), 4)
     xd, sd = dev_bf16(x), dev_scales(s, "f16")
-    for plan in [(1, 1, 10), (2, 4, 3), (1, 1, 10), (4, 4, 2), (1, 1, 1), (2, 1, 5)]:
+    for plan in [(1, 1, 10), (2, 4, 3), (1, 1, 10), (4, 4, 2), (1, 1, 1), (2, 1, 5), (2, 2, 4)]:
         out = Guarded((M, N), torch.bfloat16)
         q.qgemm_w4a16(xd, pg, sd, N, out=out.t, plan=plan, ws=ws)
         _assert_close(numerics.bf16_to_f64(host_u16(out.check(str(plan)))), ref, str(plan))

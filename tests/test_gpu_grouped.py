@@ -78,7 +78,8 @@ def test_items_match_the_oracle(bits, act, M, K, Ns):
 
 
 @pytest.mark.parametrize("bits", [4, 8])
-@pytest.mark.parametrize("M,K,N", [(1, 2560, 19456), (16, 9728, 2560), (5, 640, 320)])
+@pytest.mark.parametrize("M,K,N", [(1, 2560, 19456), (16, 9728, 2560), (5, 640, 320),
+                                   (16, 2560, 19456)])
 def test_group_of_one_is_the_single_call(bits, M, K, N):
     x, items = _group(bits, M, K, [N], 900 + M)
     dw = _dev(bits, items)
