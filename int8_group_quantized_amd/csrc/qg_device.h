@@ -116,6 +116,11 @@ struct Act<false> {   // bf16 activations and output
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
   }
+  // 32x32x16: lane L holds row / column L % 32, K slice 8 (L / 32) .. +7.
+  static __device__ __forceinline__ f32x16 mma32(const u32x4& a, const u32x4& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
   static __device__ __forceinline__ uint32_t pack2(float a, float b) { return pack_bf16x2(a, b); }
   static __device__ __forceinline__ uint16_t out(float f) { return f32_to_bf16_bits(f); }
 };
@@ -126,6 +131,10 @@ struct Act<true> {    // fp16 activations and output
   static constexpr uint32_t kOffset = 0x64086408u;   // two fp16 1032.0
   static __device__ __forceinline__ f32x4 mma(const u32x4& a, const u32x4& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x16 mma32(const u32x4& a, const u32x4& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
   }
   // Round-toward-zero pair conversion: exact for the integer codes.
