@@ -304,8 +304,8 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(2))) vo
 
 // Negated INT4 offsets: nbias[g * Mp + m] = -(c * sum_{k in g} x[m, k]) with
 // c = 136 (bf16 activations) or 1032 (fp16),
-// formed by the same 16x16x32 chain (four K steps of 32, from zero) that the
-// main kernel continues from. One wavefront per (16-row block, run of
+// formed by a 16x16x32 chain (four K steps of 32, from zero); the main
+// kernel's chains of products start from it. One wavefront per (16-row block, run of
 // kBiasGroups groups), all of its x loads issued before the first multiply;
 // rows from M to Mp repeat row M - 1.
 constexpr int kBiasGroups = 4;
