@@ -426,18 +426,18 @@ __global__ __launch_bounds__(256, 2) void swa_attention_kernel(
 // value rows. This kernel gives one workgroup a (sequence, KV head, group of
 // WV query heads, chunk of keys), one wavefront per query head, and fetches
 // every 64-key step's K and V rows (32 KB) once for the whole group, straight
-// into an LDS ring kRing steps deep by buffer loads. One more wavefront only
+// into an LDS ring of kRing slots by buffer loads. One more wavefront only
 // issues those loads (32 per step, 1 KB each): it waits for a step with a
-// constant vmcnt count and meets the others at one barrier per step. The wavefronts that compute issue
-// no memory loads inside the loop, so no wait the compiler places before
-// their LDS reads can stall on the ring. A row's 16-byte pieces are stored
+// constant vmcnt count and meets the others at one barrier per step. The
+// wavefronts that compute issue no memory loads inside the loop, so no wait
+// the compiler places before their LDS reads can stall on the ring. A row's 16-byte pieces are stored
 // XOR-swizzled by the row index, so the K operand reads (16 rows, one piece
 // each) and the transposing V^T reads (16 rows, 8 bytes each) hit distinct
 // banks. Each wavefront keeps its head's online softmax over the whole chunk,
 // so no merge runs between wavefronts; chunks merge through partial records
 // of the one-head kernel's size (O, maxima, sums per chunk and head, here in
 // the accumulators' lane order), with one arrival count per head group.
-constexpr int kRing = 2;                          // steps in flight
+constexpr int kRing = 2;                          // slots: the step computed, the next one loading
 constexpr int kRingKeys = 64;                     // keys per step
 constexpr int kRingSlot = 2 * kRingKeys * kRowBytes;   // K rows, then V rows, of one step
 constexpr int kRingLds = kRing * kRingSlot;
