@@ -105,6 +105,23 @@ def test_batch4_full_cache_plan():
     _parity(4, A["T"], A["Hq"], A["Hkv"], S, [S, 4100, 700, 16], 0, 6080)
 
 
+@pytest.mark.parametrize("B", [16, 40])
+def test_large_batch_full_cache_sampled(B):
+    # the library's plan over the full Long cache at larger batches: the
+    # shared K/V stream in four chunks (16 sequences) or in one chunk, stored
+    # without a merge (40 sequences, 160 units); sequences are independent,
+    # so four of them (a ragged one and one that is only the block among
+    # them) are checked against the oracle
+    A = workloads.ATTENTION
+    T, S = A["T"], A["context"] + A["T"]
+    lens = [S if b % 7 else 3000 for b in range(B)]
+    lens[-1] = T
+    qb, kb, vb, sc, got = _run(B, T, A["Hq"], A["Hkv"], S, lens, 0, 6090 + B)
+    pick = [0, 7, B // 2 + 1, B - 1]
+    ref = _ref(qb[pick], kb[pick], vb[pick], [lens[i] for i in pick], T, S, 0, sc)
+    _check(got[pick], ref, "B%d sampled %s" % (B, pick))
+
+
 @pytest.mark.parametrize("window", [0, 64, 256, 1024, 5, 1])
 def test_ragged_batch(window):
     # a long sequence, a medium one, one that is only the block, and one
