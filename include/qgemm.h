@@ -301,7 +301,7 @@ qg_status qgemm_w8f16_grouped(const void* x, const qg_group_item* items, int cou
  *   seq_lens  DEVICE int32 [B]; each must lie in [T, S_max] (values outside
  *             are clamped into that range, never read out of bounds)
  *   out       DEVICE bf16 [B, T, Hq, D] (must not alias the inputs)
- *   D         must be 128; 1 <= T <= 16; Hq % Hkv == 0; window >= 0
+ *   D         must be 128; 1 <= T <= 16; Hq % Hkv == 0, Hq <= 4096; window >= 0
  *   scale     the softmax scale (1/sqrt(D) in the usual model), finite
  *   workspace qg_swa_workspace_bytes(...) bytes, 16-byte aligned (NULL when
  *             that is 0); its first 64 KiB are arrival counters that must be

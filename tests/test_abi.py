@@ -207,6 +207,7 @@ def test_swa_attention_validates():
     assert _swa(L, T=17) == SHAPE
     assert _swa(L, Hq=20, Hkv=3) == SHAPE
     assert _swa(L, Hkv=0) == SHAPE
+    assert _swa(L, T=1, Hq=4104, Hkv=4) == SHAPE      # more than 4096 query heads
     assert _swa(L, S_max=8) == SHAPE                # shorter than the block
     assert _swa(L, window=-1) == SHAPE
     assert _swa(L, chunk=48) == SHAPE               # not a multiple of 32
