@@ -255,8 +255,9 @@ qg_status qg_fake_quant_w8(const void* W, qg_dtype w_dt, const void* scales,
  *   workspace qg_workspace_bytes_grouped(...) bytes, same rules as above
  * Each item's output equals what the single GEMM computes on it, bit for
  * bit when the single call and the group pick the same tiling plan; the
- * group's plan is chosen for the summed N. Errors as for qgemm_w4a16, plus
- * QG_ERR_NULL for items == NULL and QG_ERR_SHAPE for a count out of range. */
+ * group's plan is chosen for the summed N, which must also meet the limits
+ * of one N. Errors as for qgemm_w4a16, plus QG_ERR_NULL for items == NULL
+ * and QG_ERR_SHAPE for a count out of range. */
 typedef struct {
   const void* packed_w;   /* qg_packed_bytes(bits, K, N) bytes */
   const void* scales;     /* [K/128, N] */

@@ -183,6 +183,8 @@ def test_grouped_entry_points_validate():
         assert f(FAKE, _items(*([512] * 17)), 17, 1, 1, 256, 0, 0, None) == SHAPE
         assert f(FAKE, _items(512, 24), 2, 1, 1, 256, 0, 0, None) == SHAPE     # N % 16
         assert f(FAKE, _items(512), 1, 1, 1, 100, 0, 0, None) == SHAPE       # K % 128
+        # each N within limits, their sum past 2^20
+        assert f(FAKE, _items(1 << 19, 1 << 19, 16), 3, 1, 1, 128, 0, 0, None) == SHAPE
         assert f(FAKE, _items(512, 512, p=0), 2, 1, 1, 256, 0, 0, None) == NULL
         assert f(FAKE, _items(512), 1, 2, 1, 256, 0, 0, None) == DTYPE
         assert f(MIS, _items(512), 1, 1, 1, 256, 0, 0, None) == ALIGN
